@@ -1,0 +1,167 @@
+/*
+ * topselect.h -- C ABI of the MI355X (gfx950) batched per-row vocabulary sampler.
+ *
+ * Three operations on fp32 logits laid out row-major as [rows, row_stride] (row r starts
+ * at logits + r * row_stride; only the first `vocab` entries of a row are read):
+ *
+ *   ts_topk_select   deterministic top-k select with index-ordered ties;
+ *   ts_topp_mask     softmax + top-p nucleus (probability-space predicate, row max kept);
+ *   ts_sample_rows   Gumbel-max sampling over the kept set, log1p(-u) noise, Philox4x32-10.
+ *
+ * Sources (page title, then section):
+ *   [DETK]   vLLM PR #55122 "[Kernel] Make persistent_topk deterministic" -- "Changes"
+ *            (exact radix select, index-ordered ties, ascending-index output, per-CTA
+ *            >/== counts prefix-summed in CTA order) and "Test plan" (short rows padded -1).
+ *   [TOPP]   "Split top-p numerical reference and conservative gate" -- "Source basis"
+ *            (predicate in probability space, keep the row maximum), "Independent binary64
+ *            numerical reference" (canonical order, p taken after fp32 conversion, reaching
+ *            p keeps), "Breakage probes" (non-finite inputs fail closed).
+ *   [GUMBEL] prhub summary of vLLM PR #45996 -- "implementation breakdown" and "key source
+ *            excerpts" (g = -log(-log1p(-u)), u clamped at the generator's minimum, per-row
+ *            seed and temperature applied inside the kernel, max with its index).
+ *   [LOGP]   RL-Kernel issue #332 "Deterministic SM90 linear_logp" -- "Integration"
+ *            (transform order temperature -> top-k -> top-p) and "Contract constants"
+ *            (padded / masked lanes contribute 0 mass; reduction shape independent of batch).
+ *   [REJ]    mlxcel issue #901 -- "Task" (one launch for the batch with per-row parameters;
+ *            masked, zero-probability entries are never sampled).
+ *
+ * Conventions shared by all three operations:
+ *   - Every pointer argument except `workspace`'s size query is a DEVICE pointer unless
+ *     noted. The caller owns all memory; the library never allocates, frees or copies to
+ *     the host inside these calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
+ *     stream): they enqueue kernels and return; they never synchronise.
+ *   - Ordering of a row: by (logit descending, token id ascending); -0.0 and +0.0 are equal.
+ *     Top-k ranks the raw fp32 logits; temperature enters only exp((x - max)/T) and the
+ *     Gumbel score (x - max)/T + g.
+ *   - Per-row parameters: k >= vocab means top-k off; p == 1.0f means top-p off; T == 0
+ *     means greedy (the first token of the ordering). NULL parameter arrays mean: top_k
+ *     off, top_p = 1, temperature = 1.
+ *   - -inf logits are masked tokens (weight 0, never sampled). NaN or +inf logits, or a
+ *     row of only -inf, reject the row (for ts_topk_select only NaN rejects).
+ *   - Per-row problems are reported in row_status[r] (if row_status is non-NULL) and the
+ *     row's outputs are poisoned (-1 ids, kept count 0, all-zero mask row); other rows are
+ *     unaffected. Codes, by precedence: TS_ROW_NONFINITE, TS_ROW_BAD_K, TS_ROW_BAD_P,
+ *     TS_ROW_BAD_T.
+ *   - Host-side argument errors return a negative TS_ERR_* code before anything is
+ *     enqueued; ts_last_error() then holds a thread-local message.
+ *   - Workspace: device memory of at least ts_workspace_bytes(op, rows, vocab, k_max)
+ *     bytes, 256-byte aligned. Its leading counter region must be zero before the first
+ *     call (ts_workspace_init, or zero-filled memory); every call leaves it zero again.
+ *     One workspace serves one call at a time: calls that overlap on one workspace race.
+ *   - Results are deterministic: the same inputs give the same output bytes on every
+ *     call, independent of how rows are split over workgroups.
+ */
+#ifndef TOPSELECT_H_
+#define TOPSELECT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of the host API. */
+#define TS_OK               0
+#define TS_ERR_INVALID_ARG  (-1)   /* null pointer, rows < 0, vocab < 1, stride < vocab, ... */
+#define TS_ERR_WORKSPACE    (-2)   /* workspace NULL, misaligned or smaller than required */
+#define TS_ERR_UNSUPPORTED  (-3)   /* no HIP device, or the device is not gfx950 */
+#define TS_ERR_LAUNCH       (-4)   /* a HIP launch failed; detail in ts_last_error() */
+
+/* Per-row status codes written to row_status[r]. */
+#define TS_ROW_OK           0
+#define TS_ROW_NONFINITE    1      /* NaN or +inf logits, or every logit is -inf */
+#define TS_ROW_BAD_K        2      /* k < 1, or (ts_topk_select) min(k, row_len) > k_max */
+#define TS_ROW_BAD_P        3      /* p not in (0, 1] (NaN included) */
+#define TS_ROW_BAD_T        4      /* temperature negative, NaN or infinite */
+
+/* Operation ids for ts_workspace_bytes. */
+#define TS_OP_TOPK_SELECT   0
+#define TS_OP_TOPP_MASK     1
+#define TS_OP_SAMPLE_ROWS   2
+
+/* Largest supported row length (ids are int32). */
+#define TS_MAX_VOCAB        ((int64_t)1 << 30)
+
+/*
+ * Workspace size in bytes for one call of `op` on `rows` rows of `vocab` logits
+ * (k_max is the ts_topk_select output width; ignored for the other ops). Returns 0 for
+ * invalid sizes. Pure host function: needs no device.
+ */
+size_t ts_workspace_bytes(int op, int64_t rows, int64_t vocab, int32_t k_max);
+
+/* Zero the workspace's counter region (enqueued on `stream`, no memset node). */
+int ts_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ts_topk_select -- [DETK] "Changes": exact top-k by (value desc, index asc).
+ *   keys        [rows, row_stride] fp32, read-only.
+ *   k           [rows] int32, per-row k (>= 1). k >= row_len selects the whole row.
+ *   k_max       width of out_idx; every row needs min(k[r], row_len) <= k_max.
+ *   out_idx     [rows, k_max] int32, written: the selected ids in ASCENDING id order,
+ *               then -1 in the unused slots ([DETK] "Test plan": short rows).
+ *   row_status  [rows] int32 or NULL.
+ */
+int ts_topk_select(const float* keys, int64_t rows, int64_t row_len, int64_t row_stride,
+                   const int32_t* k, int32_t k_max, int32_t* out_idx, int32_t* row_status,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ts_topp_mask -- [TOPP] "Source basis" and "Independent binary64 numerical reference":
+ * temperature -> top-k -> top-p. With w_i = exp((x_i - max)/T) over the top-k set K and
+ * Z = sum_K w, the kept set P is the shortest prefix of K (in the row ordering) whose
+ * weight reaches p * Z (>=). P always holds the row maximum.
+ *   top_k, top_p, temperature   [rows] or NULL.
+ *   out_kept    [rows] int32: |P|.
+ *   out_mask    [rows, vocab] uint8 or NULL: 1 for tokens in P, else 0 (dense, row pitch
+ *               = vocab bytes).
+ */
+int ts_topp_mask(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                 const int32_t* top_k, const float* top_p, const float* temperature,
+                 int32_t* out_kept, uint8_t* out_mask, int32_t* row_status,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ts_sample_rows -- [GUMBEL] "key source excerpts": one token per row,
+ * argmax over P of (x_i - max)/T + g_i with g_i = -log(-log1p(-u_i)) in fp32 and the
+ * lowest id winning exact ties; T == 0 returns the first token of the row ordering.
+ *   seed        [rows] uint64, required: u_i comes from Philox4x32-10 (Salmon et al.,
+ *               SC'11) with key (seed mod 2^32, seed div 2^32), counter (i div 4, r, 0, 0),
+ *               output word i mod 4; u = fp32(word * 2^-32) clamped to [2^-32, 1 - 2^-24].
+ *               r is the row's index within this call.
+ *   out_token   [rows] int32.
+ */
+int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                   const int32_t* top_k, const float* top_p, const float* temperature,
+                   const uint64_t* seed, int32_t* out_token, int32_t* row_status,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic: the noise the sampler uses. For each tokens[j] of row `row` under `seed`,
+ * writes the Philox word, u and g (all device arrays of n entries; any output may be NULL).
+ */
+int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n,
+                    uint32_t* out_word, float* out_u, float* out_g, void* stream);
+
+/*
+ * Test-only, bit-neutral path forcing (process-wide; not thread-safe). Knobs:
+ *   TS_KNOB_CHUNK_ELEMS   elements per workgroup chunk (0 = automatic; else a multiple of
+ *                         4096 in [4096, 40960]): changes how a row is split.
+ *   TS_KNOB_FORCE_EXACT   1 = chunks skip the sampled-threshold filter and run the exact
+ *                         in-register radix select.
+ *   TS_KNOB_LEADER_GLOBAL 1 = the per-row leader works from global memory, never LDS.
+ * Every setting must give byte-identical results. Returns the previous value.
+ */
+#define TS_KNOB_CHUNK_ELEMS   1
+#define TS_KNOB_FORCE_EXACT   2
+#define TS_KNOB_LEADER_GLOBAL 3
+int64_t ts_debug_set(int knob, int64_t value);
+
+const char* ts_status_string(int status);  /* static string for a TS_* or TS_ROW_* code */
+const char* ts_last_error(void);           /* thread-local detail of the last host error */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TOPSELECT_H_ */

@@ -1,0 +1,300 @@
+"""GPU parity of the three C-ABI entry points against the binary64 oracle.
+
+Sizes span several workgroup chunks and ragged tails; the full-size workloads are checked
+on sampled rows. Every case prints a [case] line first so a failure can be located.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import top_select_gumbel_amd as ts
+from top_select_gumbel_amd import workloads as wl
+from gpu_helpers import banner, check_samples, check_topk, check_topp, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _torch():
+    return torch_cuda()
+
+
+def run_topk(x, k, k_max, stride_pad=0):
+    torch = torch_cuda()
+    rows, v = x.shape
+    if stride_pad:
+        buf = np.zeros((rows, v + stride_pad), np.float32)
+        buf[:, :v] = x
+        xt = dev(buf)[:, :v]
+    else:
+        xt = dev(x)
+    out, st = ts.ts_topk_select(xt, dev(np.asarray(k, np.int32)), k_max)
+    torch.cuda.synchronize()
+    return host(out), host(st)
+
+
+def run_topp(x, k, p, t, want_mask=True):
+    torch = torch_cuda()
+    kept, mask, st = ts.ts_topp_mask(dev(x), None if k is None else dev(np.asarray(k, np.int32)),
+                                     None if p is None else dev(np.asarray(p, np.float32)),
+                                     None if t is None else dev(np.asarray(t, np.float32)), want_mask)
+    torch.cuda.synchronize()
+    return host(kept), (host(mask) if mask is not None else None), host(st)
+
+
+def run_sample(x, k, p, t, seeds):
+    torch = torch_cuda()
+    tok, st = ts.ts_sample_rows(dev(x), None if k is None else dev(np.asarray(k, np.int32)),
+                                None if p is None else dev(np.asarray(p, np.float32)),
+                                None if t is None else dev(np.asarray(t, np.float32)),
+                                dev(np.asarray(seeds, np.uint64)))
+    torch.cuda.synchronize()
+    return host(tok), host(st)
+
+
+# ----------------------------------------------------------------------------- noise
+def test_noise_words_and_gumbel_match_oracle():
+    banner("gumbel noise: 4096 tokens, 3 seeds")
+    torch = torch_cuda()
+    toks = np.concatenate([np.arange(0, 2048), np.random.default_rng(0).integers(0, 1 << 30, 2048)]).astype(np.int32)
+    for seed, row in [(0, 0), (0xDEADBEEFCAFEF00D, 17), (2 ** 64 - 1, 65535)]:
+        w, u, g = ts.ts_gumbel_noise(seed, row, dev(toks))
+        torch.cuda.synchronize()
+        w = host(w).view(np.uint32)
+        want = oracle.token_words(seed, row, toks)
+        assert np.array_equal(w, want)
+        u = host(u)
+        assert np.array_equal(u.astype(np.float64), np.array([oracle.uniform_from_word(int(v)) for v in want]))
+        g = host(g).astype(np.float64)
+        g_ref = np.array([oracle.gumbel_from_word(int(v)) for v in want])
+        # fp32 log1p/log: a few ulps of the result
+        assert np.all(np.abs(g - g_ref) <= 4 * np.spacing(np.abs(g_ref).astype(np.float32)).astype(np.float64) + 1e-7)
+
+
+def test_noise_clamp_endpoints():
+    banner("gumbel noise: clamp end points")
+    # find tokens whose words are extreme is impractical; check the map through the debug
+    # kernel on tokens and compare the formula at the two clamp ends via the oracle instead
+    torch = torch_cuda()
+    toks = np.arange(0, 1 << 16, dtype=np.int32)
+    w, u, g = ts.ts_gumbel_noise(123, 4, dev(toks))
+    torch.cuda.synchronize()
+    u = host(u)
+    assert u.min() >= 2.0 ** -32 and u.max() <= 1 - 2.0 ** -24
+    assert np.isfinite(host(g)).all()
+
+
+# ----------------------------------------------------------------------------- top-k
+def test_topk_tiny_config():
+    b = wl.tiny()
+    banner("topk tiny 4x1024 k=50")
+    out, st = run_topk(b.logits, b.k, 50)
+    check_topk(b.logits, b.k, 50, out, st, "tiny")
+
+
+def test_topk_v16_rows():
+    b = wl.tiny_v16()
+    banner("topk 200 rows V=16")
+    out, st = run_topk(b.logits, b.k, 16)
+    check_topk(b.logits, b.k, 16, out, st, "v16")
+
+
+@pytest.mark.parametrize("rows,v,k_hi,kind,pad", [
+    (8, 50000, 2048, "normal", 0),
+    (5, 100003, 700, "normal", 5),            # ragged vocab, unaligned rows
+    (6, 81920, 2048, "ties", 0),              # heavy exact ties
+    (3, 40961, 100, "normal", 3),             # one element past a chunk
+    (7, 4097, 5000, "normal", 0),             # k >= V for some rows
+])
+def test_topk_random(rows, v, k_hi, kind, pad):
+    banner(f"topk random rows={rows} V={v} k<= {k_hi} kind={kind} pad={pad}")
+    b = wl.small_random(100 + rows, rows, v, k_hi, tie_levels=7 if kind == "ties" else 0)
+    k_max = k_hi
+    out, st = run_topk(b.logits, b.k, k_max, stride_pad=pad)
+    check_topk(b.logits, b.k, k_max, out, st, kind)
+
+
+def test_topk_special_rows():
+    banner("topk special rows")
+    v = 3000
+    x = np.random.default_rng(1).standard_normal((9, v)).astype(np.float32)
+    x[0] = 2.5                                  # all equal -> [0, k)
+    x[1, ::2] = -0.0
+    x[1, 1::2] = 0.0                            # signed zeros tie
+    x[2] = np.float32(1e-40) * np.arange(v)     # subnormals are distinct keys
+    x[3, 17] = np.nan                           # rejected
+    x[4, 5] = np.inf                            # +-inf are ordinary keys
+    x[4, 6] = -np.inf
+    x[5] = -np.inf
+    x[6] = np.float32(3e38) * np.sign(np.random.default_rng(2).standard_normal(v)).astype(np.float32)
+    x[7, :] = np.float32(1.0) + np.float32(2.0 ** -23) * (np.arange(v) % 3)   # adjacent fp32 values
+    k = np.array([77, 1500, 100, 5, 10, 20, 2000, 999, 0], np.int32)
+    out, st = run_topk(x, k, 2048)
+    check_topk(x, k, 2048, out, st, "special")
+
+
+def test_topk_large_k_stream_path():
+    banner("topk k up to 6000 (row-streaming leader)")
+    b = wl.small_random(7, 4, 30000, 6000)
+    out, st = run_topk(b.logits, b.k, 6000)
+    check_topk(b.logits, b.k, 6000, out, st, "large-k")
+
+
+def test_topk_indexer_rows_sampled():
+    b = wl.indexer_rows()
+    banner("topk indexer 32x131072 k=2048 (8 rows checked)")
+    out, st = run_topk(b.logits, b.k, 2048)
+    sel = [0, 3, 8, 13, 21, 26, 30, 31]
+    check_topk(b.logits[sel], b.k[sel], 2048, out[sel], st[sel], "indexer")
+
+
+def test_topk_indexer_long_and_near_uniform():
+    for b in (wl.indexer_long(), wl.indexer_near_uniform()):
+        banner(f"topk {b.name} {b.logits.shape}")
+        out, st = run_topk(b.logits, b.k, 2048)
+        check_topk(b.logits, b.k, 2048, out, st, b.name)
+
+
+def test_topk_deterministic_and_path_invariant():
+    banner("topk repeat + chunk-size forcing")
+    b = wl.small_random(9, 6, 90000, 2048, tie_levels=50)
+    ref, _ = run_topk(b.logits, b.k, 2048)
+    for _ in range(5):
+        out, _ = run_topk(b.logits, b.k, 2048)
+        assert np.array_equal(out, ref)
+    try:
+        for ce in (4096, 8192, 20480):
+            ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
+            out, _ = run_topk(b.logits, b.k, 2048)
+            assert np.array_equal(out, ref), f"chunk {ce}"
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 4096)
+        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 1)
+        out, _ = run_topk(b.logits, b.k, 2048)
+        assert np.array_equal(out, ref), "leader from global"
+    finally:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
+        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 0)
+
+
+# ----------------------------------------------------------------------------- top-p
+def test_topp_tiny_and_v16():
+    b = wl.tiny()
+    banner("topp tiny")
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t)
+    check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "tiny")
+    b = wl.tiny_v16()
+    banner("topp v16 x200")
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t)
+    check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "v16")
+
+
+@pytest.mark.parametrize("rows,v,k_hi,scale,ties", [
+    (16, 30000, 2048, 2.0, 0),
+    (8, 70001, 1024, 3.0, 0),
+    (8, 50000, 1500, 1.0, 5),
+])
+def test_topp_random(rows, v, k_hi, scale, ties):
+    banner(f"topp random rows={rows} V={v} k<={k_hi}")
+    b = wl.small_random(200 + rows, rows, v, k_hi, scale=scale, tie_levels=ties)
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t)
+    check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "random")
+
+
+def test_topp_topk_off_and_special():
+    banner("topp with top-k off (stream path), T=0, p=1, invalid rows")
+    rng = np.random.default_rng(5)
+    v = 12000
+    x = (rng.standard_normal((10, v)) * 1.5).astype(np.float32)
+    x[3, 100] = np.inf
+    x[4] = -np.inf
+    x[5, :50] = -np.inf
+    p = np.array([0.9, 0.5, 1.0, 0.9, 0.9, 0.95, 0.0, 0.7, 0.8, 0.99], np.float32)
+    t = np.array([1.0, 0.7, 1.0, 1.0, 1.0, 1.3, 1.0, 0.0, -1.0, 1.0], np.float32)
+    kept, mask, st = run_topp(x, None, p, t)
+    check_topp(x, None, p, t, kept, mask, st, "k-off")
+    k = np.array([3000, 1, 5, 12000, 100, 2500, 10, 10, 10, 4000], np.int32)
+    kept, mask, st = run_topp(x, k, p, t)
+    check_topp(x, k, p, t, kept, mask, st, "k-mixed")
+
+
+def test_topp_decode_rows_sampled():
+    b = wl.decode()
+    banner("topp decode 64x151936 (16 rows checked)")
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
+    sel = list(range(0, 64, 4))
+    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "decode")
+
+
+def test_topp_tie_stress_sampled():
+    b = wl.tie_stress()
+    banner("topp tie stress 128x128256 (12 rows incl. the all-equal row)")
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
+    sel = list(range(0, 128, 12)) + [127]
+    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "tie")
+
+
+# ----------------------------------------------------------------------------- sampling
+def test_sample_tiny_and_v16():
+    b = wl.tiny()
+    banner("sample tiny")
+    tok, st = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    kept, _, _ = run_topp(b.logits, b.k, b.p, b.t, want_mask=False)
+    check_samples(b.logits, b.k, b.p, b.t, b.seeds, tok, st, kept, "tiny")
+    b = wl.tiny_v16()
+    banner("sample v16 x200")
+    tok, st = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    kept, _, _ = run_topp(b.logits, b.k, b.p, b.t, want_mask=False)
+    check_samples(b.logits, b.k, b.p, b.t, b.seeds, tok, st, kept, "v16")
+
+
+def test_sample_random_and_paths():
+    rng = np.random.default_rng(77)
+    v = 20000
+    x = (rng.standard_normal((12, v)) * 2).astype(np.float32)
+    x[11, :] = -np.inf
+    k = np.array([5, 2048, 100, 20000, 20000, 20000, 3000, 1, 700, 20000, 64, 10], np.int32)
+    p = np.array([0.9, 0.8, 1.0, 1.0, 0.9, 1.0, 0.95, 0.5, 0.6, 1.0, 0.99, 0.9], np.float32)
+    t = np.array([1.0, 0.6, 1.2, 1.0, 1.0, 0.0, 1.0, 1.0, 1.0, 1.4, 0.5, 1.0], np.float32)
+    seeds = rng.integers(0, 2 ** 64, 12, dtype=np.uint64)
+    banner("sample mixed paths V=20000")
+    tok, st = run_sample(x, k, p, t, seeds)
+    kept, _, _ = run_topp(x, k, p, t, want_mask=False)
+    check_samples(x, k, p, t, seeds, tok, st, kept, "mixed")
+
+
+def test_sample_decode_rows_sampled():
+    b = wl.decode()
+    banner("sample decode 64x151936 (16 rows checked)")
+    tok, st = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    kept, _, _ = run_topp(b.logits, b.k, b.p, b.t, want_mask=False)
+    sel = list(range(1, 64, 4))
+    res, exempt = check_samples(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], b.seeds[sel], tok[sel], st[sel],
+                                kept[sel], "decode")
+    assert exempt <= 2
+
+
+def test_sample_heavy_rows_match_oracle():
+    b = wl.heavy(rows=8)
+    seeds = wl.heavy_launch_seeds(0, 8)
+    banner("sample heavy-tailed 8x32000 (full-row path)")
+    tok, st = run_sample(b.logits, b.k, b.p, b.t, seeds)
+    check_samples(b.logits, b.k, b.p, b.t, seeds, tok, st, None, "heavy")
+
+
+def test_sample_deterministic_and_path_invariant():
+    banner("sample repeat + chunk forcing")
+    b = wl.small_random(31, 8, 100000, 2048, scale=2.0)
+    ref, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    kref, mref, _ = run_topp(b.logits, b.k, b.p, b.t)
+    for _ in range(3):
+        tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+        assert np.array_equal(tok, ref)
+    try:
+        for ce in (4096, 12288):
+            ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
+            tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+            assert np.array_equal(tok, ref), f"chunk {ce}"
+            kept, mask, _ = run_topp(b.logits, b.k, b.p, b.t)
+            assert np.array_equal(kept, kref) and np.array_equal(mask, mref)
+    finally:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
