@@ -82,8 +82,14 @@ def check_topp(x, k, p, t, kept, mask, status, label="", max_count_mismatch=0):
     return res
 
 
-def check_samples(x, k, p, t, seeds, tokens, status, kept_gpu=None, label=""):
-    res = oracle.sample_rows(x, k, p, t, seeds)
+def check_samples(x, k, p, t, seeds, tokens, status, kept_gpu=None, label="", row_ids=None):
+    """row_ids: the rows' indices within the GPU call (the Philox counter word); default 0..n-1."""
+    ids = list(range(x.shape[0])) if row_ids is None else [int(v) for v in row_ids]
+    x = np.asarray(x, np.float32)
+    res = [oracle.sample_row(x[r], None if k is None else int(k[r]),
+                             None if p is None else oracle.to_f32(p[r]),
+                             None if t is None else oracle.to_f32(t[r]), int(seeds[r]), ids[r])
+           for r in range(x.shape[0])]
     exempt = 0
     for r, o in enumerate(res):
         assert status[r] == o.status, f"{label} row {r}: status {status[r]} vs {o.status}"
@@ -94,7 +100,7 @@ def check_samples(x, k, p, t, seeds, tokens, status, kept_gpu=None, label=""):
         if kept_gpu is not None and o.topp.kept != int(kept_gpu[r]) and (t is None or t[r] != 0):
             tv = 1.0 if t is None else oracle.to_f32(t[r])
             kept_ids = o.topp.order[: int(kept_gpu[r])]
-            want, gap = oracle.gumbel_argmax(o.topp.x, o.topp.m, tv, kept_ids, int(seeds[r]), r)
+            want, gap = oracle.gumbel_argmax(o.topp.x, o.topp.m, tv, kept_ids, int(seeds[r]), ids[r])
         if gap < GAP_EXEMPT:
             exempt += 1
             continue

@@ -269,7 +269,7 @@ def test_sample_decode_rows_sampled():
     kept, _, _ = run_topp(b.logits, b.k, b.p, b.t, want_mask=False)
     sel = list(range(1, 64, 4))
     res, exempt = check_samples(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], b.seeds[sel], tok[sel], st[sel],
-                                kept[sel], "decode")
+                                kept[sel], "decode", row_ids=sel)
     assert exempt <= 2
 
 
