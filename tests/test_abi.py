@@ -77,11 +77,11 @@ def test_bad_arguments_fail_before_any_device_work(lib):
 def test_status_strings_and_knobs(lib):
     for code in (0, -1, -2, -3, -4, 1, 2, 3, 4):
         assert lib.ts_status_string(code).decode() != "unknown status"
-    assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 12345) == -1      # not a multiple of 4096
-    old = lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 8192)
+    assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 12345) == -1      # not a multiple of 64
+    old = lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 2048)
     assert old == 0
     small = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
-    assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0) == 8192
+    assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0) == 2048
     big = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
     assert small != big
     assert lib.ts_debug_set(99, 1) == -1

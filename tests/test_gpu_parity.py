@@ -163,17 +163,22 @@ def test_topk_deterministic_and_path_invariant():
         out, _ = run_topk(b.logits, b.k, 2048)
         assert np.array_equal(out, ref)
     try:
-        for ce in (4096, 8192, 20480):
+        for ce in (1024, 2048, 4096):
             ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
             out, _ = run_topk(b.logits, b.k, 2048)
             assert np.array_equal(out, ref), f"chunk {ce}"
-        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 4096)
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 1024)
         ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 1)
         out, _ = run_topk(b.logits, b.k, 2048)
-        assert np.array_equal(out, ref), "leader from global"
+        assert np.array_equal(out, ref), "row kernel reading candidates from global"
+        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 0)
+        ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, 1)
+        out, _ = run_topk(b.logits, b.k, 2048)
+        assert np.array_equal(out, ref), "exact row-streaming path"
     finally:
         ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
         ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 0)
+        ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, 0)
 
 
 # ----------------------------------------------------------------------------- top-p
@@ -290,11 +295,13 @@ def test_sample_deterministic_and_path_invariant():
         tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
         assert np.array_equal(tok, ref)
     try:
-        for ce in (4096, 12288):
+        for ce, exact in ((1024, 0), (3072, 0), (0, 1)):
             ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
+            ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, exact)
             tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
-            assert np.array_equal(tok, ref), f"chunk {ce}"
+            assert np.array_equal(tok, ref), f"chunk {ce} exact {exact}"
             kept, mask, _ = run_topp(b.logits, b.k, b.p, b.t)
             assert np.array_equal(kept, kref) and np.array_equal(mask, mref)
     finally:
         ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
+        ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, 0)

@@ -49,35 +49,44 @@ constexpr uint32_t kKeyPosInf = 0xFF800000u;   // f2key(+inf)
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // f2key(-inf)
 
 // ---------------------------------------------------------------- wave scans
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips): Hillis-Steele
+// shifts of 1, 2, 4, 8 inside each 16-lane row, then row 0's total is broadcast into row 1
+// and row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31).
+// Lanes whose DPP source is outside the row or masked receive 0.
+#define TSD_DPP(v, ctrl, rmask, bmask) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rmask), (bmask), false))
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, 64);
-    if (lane() >= d) v += t;
-  }
+  v += TSD_DPP(v, 0x111, 0xf, 0xf);   // row_shr:1
+  v += TSD_DPP(v, 0x112, 0xf, 0xf);   // row_shr:2
+  v += TSD_DPP(v, 0x114, 0xf, 0xf);   // row_shr:4
+  v += TSD_DPP(v, 0x118, 0xf, 0xf);   // row_shr:8
+  v += TSD_DPP(v, 0x142, 0xa, 0xf);   // row_bcast:15 into rows 1 and 3
+  v += TSD_DPP(v, 0x143, 0xc, 0xf);   // row_bcast:31 into rows 2 and 3
   return v;
 }
-// Inclusive suffix sums: lane l gets sum over lanes >= l.
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+// Inclusive suffix sums: lane l gets the sum over lanes >= l.
 __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t t = __shfl_down(v, d, 64);
-    if (lane() + d < 64) v += t;
-  }
-  return v;
+  const uint32_t incl = wave_incl_scan(v);
+  return wave_total(incl) - incl + v;
 }
 __device__ __forceinline__ uint64_t wave_incl_suffix64(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint64_t t = __shfl_down(v, d, 64);
-    if (lane() + d < 64) v += t;
-  }
-  return v;
+  // two 32-bit DPP scans with the carry of the low half folded into the high half
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t lo_hi16 = lo >> 16, lo_lo16 = lo & 0xFFFFu;
+  // sums of 64 values below 2^16 stay below 2^22, so the split halves cannot overflow
+  const uint32_t s_lo16 = wave_incl_suffix(lo_lo16);
+  const uint32_t s_hi16 = wave_incl_suffix(lo_hi16);
+  const uint32_t s_hi = wave_incl_suffix(hi);
+  return ((uint64_t)s_hi << 32) + ((uint64_t)s_hi16 << 16) + (uint64_t)s_lo16;
 }
 
 // ---------------------------------------------------------------- block reductions
-// `red` is a 16-entry LDS scratch array; the function ends with a barrier so it can be
+// `red` is an NW-entry LDS scratch array (NW = waves per workgroup); the function ends with a barrier so it can be
 // reused immediately.
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
@@ -85,10 +94,11 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   bar();
   uint32_t r = red[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = max(r, red[w]);
+  for (int w = 1; w < NW; ++w) r = max(r, red[w]);
   bar();
   return r;
 }
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
@@ -96,10 +106,11 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
   bar();
   uint32_t r = red[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = min(r, red[w]);
+  for (int w = 1; w < NW; ++w) r = min(r, red[w]);
   bar();
   return r;
 }
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor(v, d, 64);
@@ -107,11 +118,12 @@ __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
   bar();
   uint32_t r = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) r |= red[w];
+  for (int w = 0; w < NW; ++w) r |= red[w];
   bar();
   return r;
 }
-// Workgroup max, min and bitwise-or of three values at once (`red` holds 48 entries).
+// Workgroup max, min and bitwise-or of three values at once (`red` holds 3 * NW entries).
+template <int NW = kWaves>
 __device__ __forceinline__ void block_reduce3(uint32_t& mx, uint32_t& mn, uint32_t& orv, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -121,18 +133,19 @@ __device__ __forceinline__ void block_reduce3(uint32_t& mx, uint32_t& mn, uint32
   }
   if (lane() == 0) {
     red[wave()] = mx;
-    red[kWaves + wave()] = mn;
-    red[2 * kWaves + wave()] = orv;
+    red[NW + wave()] = mn;
+    red[2 * NW + wave()] = orv;
   }
   bar();
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     mx = max(mx, red[w]);
-    mn = min(mn, red[kWaves + w]);
-    orv |= red[2 * kWaves + w];
+    mn = min(mn, red[NW + w]);
+    orv |= red[2 * NW + w];
   }
   bar();
 }
+template <int NW = kWaves>
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += (uint64_t)__shfl_xor(v, d, 64);
@@ -140,18 +153,41 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
   bar();
   uint64_t r = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) r += red[w];
+  for (int w = 0; w < NW; ++w) r += red[w];
   bar();
   return r;
 }
+// Workgroup sums of two 64-bit values at once (`red` holds 2 * NW entries).
+template <int NW = kWaves>
+__device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_t* red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a += (uint64_t)__shfl_xor(a, d, 64);
+    b += (uint64_t)__shfl_xor(b, d, 64);
+  }
+  if (lane() == 0) {
+    red[wave()] = a;
+    red[NW + wave()] = b;
+  }
+  bar();
+  a = 0;
+  b = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    a += red[w];
+    b += red[NW + w];
+  }
+  bar();
+}
 // Exclusive prefix over the workgroup in thread order; `total` gets the sum of all.
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
   uint32_t incl = wave_incl_scan(v);
   if (lane() == 63) red[wave()] = incl;
   bar();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     uint32_t t = red[w];
     base += (w < wave()) ? t : 0u;
     tot += t;
@@ -163,6 +199,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
 
 // Argmax over the workgroup of (score, lowest id): every thread gets the winning id and
 // (through best_s) its score.
+template <int NW = kWaves>
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
                                                 float* best_s = nullptr) {
 #pragma unroll
@@ -178,7 +215,7 @@ __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds
   float bs = reds[0];
   int32_t bi = redi[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
+  for (int w = 1; w < NW; ++w) {
     float os = reds[w];
     int32_t oi = redi[w];
     bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
