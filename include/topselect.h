@@ -46,9 +46,9 @@
  *   - Host-side argument errors return a negative TS_ERR_* code before anything is
  *     enqueued; ts_last_error() then holds a thread-local message.
  *   - Workspace: device memory of at least ts_workspace_bytes(op, rows, vocab, k_max)
- *     bytes, 256-byte aligned. Its leading counter region must be zero before the first
- *     call (ts_workspace_init, or zero-filled memory); every call leaves it zero again.
- *     One workspace serves one call at a time: calls that overlap on one workspace race.
+ *     bytes, 256-byte aligned, owned by the caller. It needs no initialisation: every call
+ *     writes what it later reads (per-wave chunk summaries, then candidate slices). One
+ *     workspace serves one call at a time: calls that overlap on one workspace race.
  *   - Results are deterministic: the same inputs give the same output bytes on every
  *     call, independent of how rows are split over workgroups.
  */
@@ -91,7 +91,8 @@ extern "C" {
  */
 size_t ts_workspace_bytes(int op, int64_t rows, int64_t vocab, int32_t k_max);
 
-/* Zero the workspace's counter region (enqueued on `stream`, no memset node). */
+/* Zero-fill a workspace (enqueued on `stream` as a fill kernel, no memset node). Optional:
+ * the operations need no initialised workspace; this only makes its contents defined. */
 int ts_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -146,16 +147,16 @@ int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n
 
 /*
  * Test-only, bit-neutral path forcing (process-wide; not thread-safe). Knobs:
- *   TS_KNOB_CHUNK_ELEMS   elements per workgroup chunk (0 = automatic; else a multiple of
- *                         4096 in [4096, 40960]): changes how a row is split.
- *   TS_KNOB_FORCE_EXACT   1 = chunks skip the sampled-threshold filter and run the exact
- *                         in-register radix select.
- *   TS_KNOB_LEADER_GLOBAL 1 = the per-row leader works from global memory, never LDS.
- * Every setting must give byte-identical results. Returns the previous value.
+ *   TS_KNOB_CHUNK_ELEMS   logits per stream-kernel chunk (0 = automatic, 8192 at most;
+ *                         else a multiple of 64 in [64, 8192]): changes how a row is split
+ *                         over workgroups. Also changes ts_workspace_bytes.
+ *   TS_KNOB_FORCE_EXACT   1 = every top-k / top-p row takes the exact row-streaming path of
+ *                         the row kernel instead of the certified candidate path.
+ * Every setting gives byte-identical results. Returns the previous value, or -1 for an
+ * unknown knob or an invalid value (the setting is then unchanged).
  */
 #define TS_KNOB_CHUNK_ELEMS   1
 #define TS_KNOB_FORCE_EXACT   2
-#define TS_KNOB_LEADER_GLOBAL 3
 int64_t ts_debug_set(int knob, int64_t value);
 
 const char* ts_status_string(int status);  /* static string for a TS_* or TS_ROW_* code */

@@ -134,7 +134,7 @@ def test_topk_special_rows():
 
 
 def test_topk_large_k_stream_path():
-    banner("topk k up to 6000 (row-streaming leader)")
+    banner("topk k up to 6000 (row-streaming path)")
     b = wl.small_random(7, 4, 30000, 6000)
     out, st = run_topk(b.logits, b.k, 6000)
     check_topk(b.logits, b.k, 6000, out, st, "large-k")
@@ -163,21 +163,18 @@ def test_topk_deterministic_and_path_invariant():
         out, _ = run_topk(b.logits, b.k, 2048)
         assert np.array_equal(out, ref)
     try:
-        for ce in (1024, 2048, 4096):
+        # 64- and 256-element chunks give more wave slices than the row kernel indexes and
+        # take the exact row-streaming path; the others the candidate path
+        for ce in (64, 256, 1024, 2048, 4096, 8192):
             ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
             out, _ = run_topk(b.logits, b.k, 2048)
             assert np.array_equal(out, ref), f"chunk {ce}"
-        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 1024)
-        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 1)
-        out, _ = run_topk(b.logits, b.k, 2048)
-        assert np.array_equal(out, ref), "row kernel reading candidates from global"
-        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 0)
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
         ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, 1)
         out, _ = run_topk(b.logits, b.k, 2048)
         assert np.array_equal(out, ref), "exact row-streaming path"
     finally:
         ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
-        ts.ts_debug_set(ts.TS_KNOB_LEADER_GLOBAL, 0)
         ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, 0)
 
 
@@ -295,7 +292,7 @@ def test_sample_deterministic_and_path_invariant():
         tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
         assert np.array_equal(tok, ref)
     try:
-        for ce, exact in ((1024, 0), (3072, 0), (0, 1)):
+        for ce, exact in ((256, 0), (1024, 0), (3072, 0), (0, 1)):
             ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, ce)
             ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, exact)
             tok, _ = run_sample(b.logits, b.k, b.p, b.t, b.seeds)

@@ -2,26 +2,33 @@
 //
 // Every call enqueues two kernels on the caller's stream:
 //
-//   ts_stream_kernel  rows x chunks workgroups of 256 threads. Each workgroup streams one
-//                     contiguous chunk (<= 8192 logits) of one row from HBM exactly once,
-//                     keeping the chunk's ordered keys in registers, and publishes a small
-//                     summary of it. While the chunk arrives it builds a 12-bit histogram of
-//                     the keys; from it the chunk picks a threshold L_c, the lower edge of
-//                     the bin holding its m_c-th largest key, with m_c a safety multiple of
-//                     the chunk's share of k, and writes every key >= L_c (id order) as a
-//                     candidate.
-//   ts_row_kernel     one 1024-thread workgroup per row. From the candidates it selects the
-//                     row's exact top-k and certifies it: if the smallest selected key is
-//                     >= every chunk's L_c, every row element that could rank above it is a
-//                     candidate, so the candidate top-k IS the row top-k. Otherwise (adversarial
-//                     or tie-heavy rows) it falls back to the exact row-streaming path. Then
-//                     the top-p mass cut and the Gumbel argmax run on the top-k set.
+//   ts_stream_kernel  rows x chunks workgroups of 256 threads (4 waves). Each workgroup streams
+//                     one contiguous chunk (<= 8192 logits) of one row from HBM exactly once and
+//                     keeps it in registers. A 2048-bin histogram of a quarter of the chunk (the
+//                     first two load slots of every wave) gives a threshold L_c: the lower edge
+//                     of the bin holding the sample's j-th largest key, j a safety multiple of
+//                     the chunk's share of k. Every wave then works alone (no further
+//                     barriers): it stages the float4 quads whose maximum reaches L_c, extracts
+//                     their elements >= L_c in id order and stores them as candidates in its own
+//                     slice of the workspace, with a 32-byte summary (count, L_c, maximum, NaN
+//                     and overflow flags).
+//   ts_row_kernel     one 512-thread workgroup per row. It gathers the row's candidates into
+//                     LDS, selects their exact top-k, and certifies it: when the smallest
+//                     selected key is >= every L_c, every row element that could rank above it
+//                     is a candidate, so the candidate top-k IS the row top-k. Otherwise
+//                     (adversarial or tie-heavy rows) it falls back to the exact row-streaming
+//                     path. Then the top-p mass cut and the Gumbel argmax run on the top-k set.
+//
+// The stream kernel is bound by vector-ALU issue as much as by HBM: a wave64 VALU instruction
+// occupies its SIMD for four cycles, so the per-element work between the loads and the
+// candidate stores is a handful of instructions per float4 (one three-input max chain, two
+// unordered compares, one threshold compare, a ballot).
 //
 // Row paths (chosen per row on the device from that row's k, p, T):
 //   CAND    k_eff <= 2048: candidates + certified selection as above.
 //   GREEDY  T == 0: the first token of the row ordering (max key, lowest id).
-//   FULL    top-k and top-p both off (sampling): each chunk computes its Gumbel argmax
-//           relative to its own maximum; the row kernel folds the chunk winners.
+//   FULL    top-k and top-p both off (sampling): each wave computes its Gumbel argmax relative
+//           to its own maximum; the row kernel folds the wave winners.
 //   STREAM  everything else (k > 2048, top-p with top-k off, failed certification): the row
 //           kernel re-reads the row from global memory once per radix pass.
 //   NONE    invalid row: outputs poisoned.
@@ -62,28 +69,32 @@ constexpr int kS1 = 8;                              // float4 loads per thread
 constexpr int kChunkMax = kT1 * 4 * kS1;            // 8192 logits per chunk
 constexpr int kHBits = 11;                          // sample histogram digit (top key bits)
 constexpr int kHBins = 1 << kHBits;
+constexpr int kHWords = kHBins + kHBins / 8;        // padded: 4 spare words after every 32 bins
 constexpr int kSampleSlots = 2;                     // slots whose keys form the sample
-constexpr int kCapMax = 4096;                       // candidate slots per chunk
-constexpr int kWStage = 512;                        // candidates staged per wave in LDS
+constexpr int kQStage = 128;                        // staged quads per wave
+constexpr int kCapW = 512;                          // candidate slots per wave in the workspace
 // row kernel
+constexpr int kRT = 512;                            // threads per row workgroup
+constexpr int kRW = kRT / 64;
 constexpr int kFastK = 2048;                        // largest k taking the candidate path
-constexpr int kBins = 256;                          // radix digit of 8 bits
-constexpr int kCC = 8;                              // replicated count histograms
-constexpr int kMC = 4;                              // replicated mass histograms
-constexpr int kLdsCand = 8192;                      // candidates the row kernel keeps in LDS
+constexpr int kDBits = 11;                          // radix digit of the row selects
+constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel thread
+constexpr int kLdsCand = 6144;                      // candidates the row kernel holds in LDS
+constexpr int kMaxSeg = 2 * kRT;                    // wave slices per row the gather indexes
+static_assert(kDBins == 4 * kRT, "each row-kernel thread owns four histogram bins");
 
-struct ChunkInfo {
-  uint32_t count;     // candidates written (CAND), capped at the chunk capacity
-  uint32_t thr;       // L_c: every key >= thr of the chunk is a candidate (0: all)
-  uint32_t kmax;      // largest key of the chunk's elements (0 if none)
-  uint32_t kmin;      // smallest key of the chunk's elements (0xFFFFFFFF if none)
+// Summary of one wave's share of a chunk (32 bytes).
+struct WaveInfo {
+  uint32_t count;     // candidates stored (CAND), capped at the slice capacity
+  uint32_t thr;       // L_c as a key: every key >= thr of the wave's elements is a candidate
+  uint32_t kmax;      // largest key among the wave's elements
+  uint32_t flags;     // bit 0: NaN seen; bit 1: candidates overflowed the slice
   uint32_t kmax_idx;  // lowest id holding kmax (GREEDY)
-  uint32_t flags;     // bit 0: NaN seen; bit 1: candidates overflowed the capacity
-  float best_s;       // FULL sampling: best score relative to the chunk maximum
+  float best_s;       // FULL sampling: best score relative to kmax's value
   int32_t best_idx;
-  uint32_t cmin;      // smallest candidate key written (0xFFFFFFFF if none)
+  uint32_t pad;
 };
-static_assert(sizeof(ChunkInfo) == 36, "ChunkInfo layout");
+static_assert(sizeof(WaveInfo) == 32, "WaveInfo layout");
 constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -99,17 +110,15 @@ struct Params {
   int32_t k_max;
   int32_t chunks;
   int32_t chunk_len;
-  int32_t cap_c;
+  int32_t cap_w;
   int32_t xcd_map;
   int32_t force_exact;
-  int32_t leader_global;
-  int32_t pad_;
   int32_t* out_idx;
   int32_t* out_kept;
   uint8_t* out_mask;
   int32_t* out_token;
   int32_t* status;
-  ChunkInfo* info;
+  WaveInfo* info;
   uint2* cand;
 };
 
@@ -121,34 +130,33 @@ struct RowPlan {
   int32_t bad;
 };
 
-// LDS of the row kernel
+// LDS of the row kernel (about 148 KB; one workgroup per CU)
 struct Smem {
-  // two histogram buffers: a pass fills one while the previous pass's one is cleared
-  uint32_t hist[2][kBins * kCC];
-  uint64_t mhist[2][kBins * kMC * 2];
-  uint2 cand[kLdsCand];
-  uint2 kset[kFastK];
-  uint32_t red[kWaves];
-  uint32_t red3[3 * kWaves];
-  uint64_t red64[2 * kWaves];
-  float reds[kWaves];
-  int32_t redi[kWaves];
-  uint32_t wave_tot[kWaves];
+  uint32_t ckey[kLdsCand];     // candidates (id order), keys and ids in separate arrays
+  uint32_t cidx[kLdsCand];
+  alignas(16) uint32_t hist[kDBins];   // count histogram; each thread reads and re-zeroes its own bins
+  alignas(16) uint64_t mhi[kDBins];    // mass histogram (fixed-point halves)
+  alignas(16) uint64_t mlo[kDBins];
+  uint32_t kkey[kFastK];       // the top-k set K
+  uint32_t kidx[kFastK];
+  uint64_t kmhi[kFastK];       // fixed-point weights of K
+  uint64_t kmlo[kFastK];
+  uint32_t segoff[kMaxSeg + 1];
+  uint32_t red[4 * kRW];
+  uint64_t red64[2 * kRW];
+  float reds[kRW];
+  int32_t redi[kRW];
   uint32_t res[4];
   uint64_t res64[4];
-  uint32_t segoff[1025];
-  uint32_t kcount;
+  uint32_t kcount[2];
 };
 
-// LDS of the stream kernel
+// LDS of the stream kernel (about 28 KB)
 struct Smem1 {
-  uint32_t hist[kHBins];
-  uint2 stage[kW1][kWStage];
-  uint32_t red3[3 * kW1];
-  uint32_t red[kW1];
-  float reds[kW1];
-  int32_t redi[kW1];
-  uint32_t wave_tot[kW1];
+  uint32_t hist[kHWords];      // sample keys by their top 11 bits
+  uint32_t hist2[kHWords];     // sample keys inside the chosen bin, by their next 11 bits
+  uint4 stage_v[kW1][kQStage];
+  uint32_t stage_q[kW1][kQStage];
   uint32_t res[4];
 };
 
@@ -189,98 +197,102 @@ __device__ __forceinline__ bool sel_member(const Sel& s, uint32_t rk, uint32_t i
 __device__ __forceinline__ Sel sel_all() { return Sel{0u, 32, 0xFFFFFFFFu}; }
 
 // ------------------------------------------------------------------ threshold-bin searches
-// Wave 0 only. Finds the highest bin b with (sum of counts in bins >= b) >= thr and writes
-// res[0] = b, res[1] = count in bins > b, res[2] = count in b.
-__device__ __forceinline__ void search_count(Smem& sm, int hb, uint32_t thr) {
-  const int l = lane();
-  uint32_t c[4];
+// Workgroup-wide searches over the kDBins-bin histograms; thread t owns bins 4t..4t+3 (one
+// conflict-free 16-byte LDS read), reads them and zeroes them for the next pass (no other
+// thread touches them before the next pass's atomics, which follow two barriers).
+//
+// Count: the highest bin b with (count in bins >= b) >= need. Writes res[0] = b,
+// res[1] = count in bins > b, res[2] = count in b. Requires 1 <= need <= total.
+__device__ __forceinline__ void search_count(Smem& sm, uint32_t need) {
+  uint4* h4 = reinterpret_cast<uint4*>(sm.hist) + threadIdx.x;
+  const uint4 v = *h4;
+  *h4 = make_uint4(0, 0, 0, 0);
+  const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t lsum = v.x + v.y + v.z + v.w;
+  const uint32_t sfx = wave_incl_suffix(lsum);     // lanes >= this one, within the wave
+  if (lane() == 0) sm.red[wave()] = sfx;
+  bar();
+  uint32_t above = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int cp = 0; cp < kCC; ++cp) s += sm.hist[hb][(4 * l + j) * kCC + cp];
-    c[j] = s;
-  }
-  const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
-  const uint32_t excl = wave_incl_suffix(lsum) - lsum;
-  const uint64_t bal = __ballot(excl + lsum >= thr);
-  const int L = bal ? 63 - __clzll((long long)bal) : -1;
-  if (l == L) {
+  for (int w = 0; w < kRW; ++w) above += (w > wave()) ? sm.red[w] : 0u;
+  const uint32_t excl = above + sfx - lsum;        // count in bins above this thread's bins
+  if (excl < need && excl + lsum >= need) {
     uint32_t acc = excl;
     int j = 3;
     for (; j > 0; --j) {
-      if (acc + c[j] >= thr) break;
+      if (acc + c[j] >= need) break;
       acc += c[j];
     }
-    sm.res[0] = 4 * L + j;
+    sm.res[0] = 4 * threadIdx.x + j;
     sm.res[1] = acc;
     sm.res[2] = c[j];
   }
+  bar();
 }
 
-// Mass version: masses are exact (hi, lo) sums, compared with `target` after conversion to
-// binary64. ma = mass already known to lie above the current prefix. Writes res[0] = bin,
-// res[1] = count above, res[2] = count in bin, res64[0..1] = ma + mass above the bin,
-// res64[2..3] = mass of the bin.
-__device__ __forceinline__ void search_mass(Smem& sm, int hb, double target, uint64_t ma_hi, uint64_t ma_lo, int S) {
-  const int l = lane();
-  uint32_t c[4];
+// Mass: the highest bin b with ma + (mass in bins >= b) >= target, masses exact (hi, lo)
+// sums compared after conversion to binary64. Writes res[0] = b, res[1] = count above,
+// res[2] = count in b, res64[0..1] = ma + mass above b, res64[2..3] = mass of b.
+__device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t ma_hi, uint64_t ma_lo, int S) {
+  const int t = threadIdx.x;
+  uint4* h4 = reinterpret_cast<uint4*>(sm.hist) + t;
+  const uint4 cv = *h4;
+  *h4 = make_uint4(0, 0, 0, 0);
   uint64_t mh[4], ml[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int cp = 0; cp < kCC; ++cp) s += sm.hist[hb][(4 * l + j) * kCC + cp];
-    c[j] = s;
-    uint64_t h = 0, o = 0;
-#pragma unroll
-    for (int cp = 0; cp < kMC; ++cp) {
-      h += sm.mhist[hb][((4 * l + j) * kMC + cp) * 2];
-      o += sm.mhist[hb][((4 * l + j) * kMC + cp) * 2 + 1];
-    }
-    mh[j] = h;
-    ml[j] = o;
+    mh[j] = sm.mhi[4 * t + j];
+    ml[j] = sm.mlo[4 * t + j];
   }
-  const uint32_t lc = c[0] + c[1] + c[2] + c[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sm.mhi[4 * t + j] = 0;
+    sm.mlo[4 * t + j] = 0;
+  }
+  const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
+  const uint32_t lc = cv.x + cv.y + cv.z + cv.w;
   const uint64_t lh = mh[0] + mh[1] + mh[2] + mh[3];
-  const uint64_t lo_ = ml[0] + ml[1] + ml[2] + ml[3];
-  const uint32_t xc = wave_incl_suffix(lc) - lc;
-  const uint64_t xh = wave_incl_suffix64(lh) - lh;
-  const uint64_t xl = wave_incl_suffix64(lo_) - lo_;
-  const bool has = mass_to_double(ma_hi + xh + lh, ma_lo + xl + lo_, S) >= target;
-  const uint64_t bal = __ballot(has);
-  const int L = bal ? 63 - __clzll((long long)bal) : -1;
-  if (l == L) {
-    uint64_t ah = ma_hi + xh, al = ma_lo + xl;
-    uint32_t ac = xc;
+  const uint64_t ll = ml[0] + ml[1] + ml[2] + ml[3];
+  const uint32_t sc = wave_incl_suffix(lc);
+  const uint64_t sh = wave_incl_suffix64(lh);
+  const uint64_t sl = wave_incl_suffix64(ll);
+  if (lane() == 0) {
+    sm.red[wave()] = sc;
+    sm.red64[wave()] = sh;
+    sm.red64[kRW + wave()] = sl;
+  }
+  bar();
+  uint32_t ac = 0;
+  uint64_t ah = 0, al = 0;
+#pragma unroll
+  for (int w = 0; w < kRW; ++w) {
+    const bool up = w > wave();
+    ac += up ? sm.red[w] : 0u;
+    ah += up ? sm.red64[w] : 0ull;
+    al += up ? sm.red64[kRW + w] : 0ull;
+  }
+  uint32_t xc = ac + sc - lc;
+  uint64_t xh = ma_hi + ah + sh - lh;
+  uint64_t xl = ma_lo + al + sl - ll;
+  const bool below = mass_to_double(xh, xl, S) < target;
+  const bool reach = mass_to_double(xh + lh, xl + ll, S) >= target;
+  if (below && reach) {
     int j = 3;
     for (; j > 0; --j) {
-      if (mass_to_double(ah + mh[j], al + ml[j], S) >= target) break;
-      ah += mh[j];
-      al += ml[j];
-      ac += c[j];
+      if (mass_to_double(xh + mh[j], xl + ml[j], S) >= target) break;
+      xh += mh[j];
+      xl += ml[j];
+      xc += c[j];
     }
-    sm.res[0] = 4 * L + j;
-    sm.res[1] = ac;
+    sm.res[0] = 4 * t + j;
+    sm.res[1] = xc;
     sm.res[2] = c[j];
-    sm.res64[0] = ah;
-    sm.res64[1] = al;
+    sm.res64[0] = xh;
+    sm.res64[1] = xl;
     sm.res64[2] = mh[j];
     sm.res64[3] = ml[j];
   }
-}
-
-// Zero histogram buffer hb (count and mass); called by waves 1..15 while wave 0 searches
-// the other buffer, or by the whole workgroup (first = 0, step = kThreads).
-__device__ __forceinline__ void clear_hist(Smem& sm, int hb, int first, int step) {
-  uint4* h = reinterpret_cast<uint4*>(sm.hist[hb]);
-  for (int i = first; i < kBins * kCC / 4; i += step) h[i] = make_uint4(0, 0, 0, 0);
-  uint4* m = reinterpret_cast<uint4*>(sm.mhist[hb]);
-  for (int i = first; i < kBins * kMC; i += step) m[i] = make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ void search_or_clear_count(Smem& sm, int hb, uint32_t thr) {
-  if (wave() == 0) search_count(sm, hb, thr);
-  else clear_hist(sm, hb ^ 1, (int)threadIdx.x - 64, kThreads - 64);
+  bar();
 }
 
 // ------------------------------------------------------------------ exact count select
@@ -288,31 +300,29 @@ __device__ __forceinline__ void search_or_clear_count(Smem& sm, int hb, uint32_t
 // yields (vis(f) calls f(rk, idx) for this thread's items; the union over threads must be
 // n_in_play items with hi_rk >= rk >= lo_rk). Bits above the highest bit where hi_rk and
 // lo_rk differ are common and skipped. A pass stops early when the threshold bin holds
-// exactly the slots still unfilled ([DETK] "Changes": pass skipping).
+// exactly the slots still unfilled ([DETK] "Changes": pass skipping). The count histogram
+// is zero on entry and on return.
 // On return: items with shr(rk, lo) > prefix are selected; eq_take of the tie_cnt items with
 // shr(rk, lo) == prefix must still be taken (lowest ids first).
 template <class Vis>
 __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint32_t n_in_play, uint32_t hi_rk,
-                             uint32_t lo_rk, Smem& sm, int& hb, uint32_t& prefix, int& lo,
-                             uint32_t& eq_take, uint32_t& tie_cnt) {
+                                             uint32_t lo_rk, Smem& sm, uint32_t& prefix, int& lo,
+                                             uint32_t& eq_take, uint32_t& tie_cnt) {
   lo = (hi_rk == lo_rk) ? 0 : 32 - __clz((int)(hi_rk ^ lo_rk));
   prefix = shr(hi_rk, lo);
   tie_cnt = n_in_play;
   while (lo > 0 && need > 0) {
-    const int d = min(8, lo);
+    const int d = min(kDBits, lo);
     const int sh = lo - d;
     const uint32_t dm = (1u << d) - 1u;
     const uint32_t pre = prefix;
     const int lo_now = lo;
-    const uint32_t copy = (uint32_t)lane() & (kCC - 1);
-    uint32_t* hist = sm.hist[hb];   // zero on entry
-    vis([&](uint32_t rk, uint32_t idx) {
-      if (shr(rk, lo_now) == pre) atomicAdd(&hist[((rk >> sh) & dm) * kCC + copy], 1u);
+    uint32_t* hist = sm.hist;
+    vis([&](uint32_t rk, uint32_t) {
+      if (shr(rk, lo_now) == pre) atomicAdd(&hist[(rk >> sh) & dm], 1u);
     });
     bar();
-    search_or_clear_count(sm, hb, need);
-    bar();
-    hb ^= 1;
+    search_count(sm, need);
     const uint32_t bin = sm.res[0], above = sm.res[1], cnt = sm.res[2];
     need -= above;
     prefix = (prefix << d) | bin;
@@ -327,10 +337,10 @@ __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint
 // idx_lo / idx_hi bound the ids of the items.
 template <class Vis>
 __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32_t n_in_play, uint32_t hi_key,
-                           uint32_t lo_key, uint32_t idx_lo, uint32_t idx_hi, Smem& sm, int& hb) {
+                                           uint32_t lo_key, uint32_t idx_lo, uint32_t idx_hi, Smem& sm) {
   Sel s;
   uint32_t eq_take, tie_cnt;
-  count_select(vis, need, n_in_play, hi_key, lo_key, sm, hb, s.prefix, s.lo, eq_take, tie_cnt);
+  count_select(vis, need, n_in_play, hi_key, lo_key, sm, s.prefix, s.lo, eq_take, tie_cnt);
   s.cutoff = 0xFFFFFFFFu;
   if (eq_take < tie_cnt) {
     // the eq_take lowest ids among the tied items: select on ~id
@@ -343,7 +353,7 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
     };
     uint32_t p2, e2, t2;
     int lo2;
-    count_select(tvis, eq_take, tie_cnt, ~idx_lo, ~idx_hi, sm, hb, p2, lo2, e2, t2);
+    count_select(tvis, eq_take, tie_cnt, ~idx_lo, ~idx_hi, sm, p2, lo2, e2, t2);
     s.cutoff = ~shl(p2, lo2);
   }
   return s;
@@ -352,42 +362,36 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
 // ------------------------------------------------------------------ mass select (top-p)
 // Smallest prefix of the row ordering whose exact fixed-point mass reaches `target`
 // ([TOPP] "Independent binary64 numerical reference", steps 4-5, with the predicate kept in
-// probability space, [TOPP] "Source basis"). vis(f) calls f(rk, idx) for items of K; wfn(rk)
-// returns the item's weight. Result: Sel of the kept set P (a canonical prefix) and |P|.
-template <class Vis, class WFn>
-__device__ __forceinline__ Sel select_mass(const Vis& vis, const WFn& wfn, double target, int S, uint32_t n_in_play,
-                           uint32_t hi_key, uint32_t lo_key, uint32_t idx_lo, uint32_t idx_hi,
-                           Smem& sm, int& hb, uint32_t& kept) {
+// probability space, [TOPP] "Source basis"). mvis(f) calls f(rk, idx, hi, lo) for this
+// thread's items of K with their fixed-point weight; wmass(rk) returns the weight of a key.
+// Result: Sel of the kept set P (a canonical prefix) and |P| in `kept`. Both histograms are
+// zero on entry and on return.
+template <class MVis, class WMass>
+__device__ __forceinline__ Sel select_mass(const MVis& mvis, const WMass& wmass, double target, int S,
+                                           uint32_t n_in_play, uint32_t hi_key, uint32_t lo_key,
+                                           uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept) {
   int lo = (hi_key == lo_key) ? 0 : 32 - __clz((int)(hi_key ^ lo_key));
   uint32_t prefix = shr(hi_key, lo);
   uint32_t n_above = 0, tie_cnt = n_in_play;
   uint64_t ma_hi = 0, ma_lo = 0, bin_hi = 0, bin_lo = 0;
   bool single = false, ran = false;
   while (lo > 0) {
-    const int d = min(8, lo);
+    const int d = min(kDBits, lo);
     const int sh = lo - d;
     const uint32_t dm = (1u << d) - 1u;
     const uint32_t pre = prefix;
     const int lo_now = lo;
     ran = true;
-    const uint32_t cc = (uint32_t)lane() & (kCC - 1);
-    const uint32_t mc = (uint32_t)lane() & (kMC - 1);
-    uint32_t* hist = sm.hist[hb];      // both zero on entry
-    uint64_t* mhist = sm.mhist[hb];
-    vis([&](uint32_t rk, uint32_t idx) {
+    mvis([&](uint32_t rk, uint32_t, uint64_t hi, uint64_t lo_m) {
       if (shr(rk, lo_now) == pre) {
         const uint32_t b = (rk >> sh) & dm;
-        const Mass m = mass_of(wfn(rk), S);
-        atomicAdd(&hist[b * kCC + cc], 1u);
-        atomicAdd((unsigned long long*)&mhist[(b * kMC + mc) * 2], (unsigned long long)m.hi);
-        atomicAdd((unsigned long long*)&mhist[(b * kMC + mc) * 2 + 1], (unsigned long long)m.lo);
+        atomicAdd(&sm.hist[b], 1u);
+        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)hi);
+        atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)lo_m);
       }
     });
     bar();
-    if (wave() == 0) search_mass(sm, hb, target, ma_hi, ma_lo, S);
-    else clear_hist(sm, hb ^ 1, (int)threadIdx.x - 64, kThreads - 64);
-    bar();
-    hb ^= 1;
+    search_mass(sm, target, ma_hi, ma_lo, S);
     const uint32_t bin = sm.res[0];
     n_above += sm.res[1];
     tie_cnt = sm.res[2];
@@ -409,7 +413,7 @@ __device__ __forceinline__ Sel select_mass(const Vis& vis, const WFn& wfn, doubl
       qh = bin_hi / tie_cnt;
       ql = bin_lo / tie_cnt;
     } else {  // every in-play key is equal and no pass ran
-      const Mass q1 = mass_of(wfn(prefix), S);
+      const Mass q1 = wmass(prefix);
       qh = q1.hi;
       ql = q1.lo;
     }
@@ -426,13 +430,13 @@ __device__ __forceinline__ Sel select_mass(const Vis& vis, const WFn& wfn, doubl
     const uint32_t pre = prefix;
     const int lo_ = lo;
     auto tvis = [&](auto f) {
-      vis([&](uint32_t rk, uint32_t idx) {
+      mvis([&](uint32_t rk, uint32_t idx, uint64_t, uint64_t) {
         if (shr(rk, lo_) == pre) f(~idx, idx);
       });
     };
     uint32_t p2, e2, t2;
     int lo2;
-    count_select(tvis, take, tie_cnt, ~idx_lo, ~idx_hi, sm, hb, p2, lo2, e2, t2);
+    count_select(tvis, take, tie_cnt, ~idx_lo, ~idx_hi, sm, p2, lo2, e2, t2);
     s.cutoff = ~shl(p2, lo2);
   }
   kept = n_above + take;
@@ -460,7 +464,7 @@ __device__ __forceinline__ int bitlen(uint32_t n) { return n ? 32 - __clz((int)n
 template <int E, class Get, class Mem, class Out>
 __device__ __forceinline__ void emit_ordered(uint32_t n, const Get& get, const Mem& mem, const Out& out,
                                              uint32_t& run, Smem& sm) {
-  for (uint32_t base = 0; base < n; base += kThreads * E) {
+  for (uint32_t base = 0; base < n; base += kRT * E) {
     uint32_t rk[E], idx[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -478,7 +482,7 @@ __device__ __forceinline__ void emit_ordered(uint32_t n, const Get& get, const M
       cnt += sel[e] ? 1u : 0u;
     }
     uint32_t tot;
-    uint32_t pos = block_excl_scan(cnt, sm.red, tot);
+    uint32_t pos = block_excl_scan<kRW>(cnt, sm.red, tot);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (sel[e]) out(run + pos++, idx[e]);
@@ -487,39 +491,53 @@ __device__ __forceinline__ void emit_ordered(uint32_t n, const Get& get, const M
   }
 }
 
-// Visit items [0, n) of an indexable source, U per thread per round with all loads of a
-// round issued first, so global-memory latency is paid once per round, not once per item.
-template <int U, class Get, class F>
-__device__ __forceinline__ void batched_for(uint32_t n, const Get& get, F f) {
-  for (uint32_t base = 0; base < n; base += kThreads * U) {
-    uint2 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t j = base + u * kThreads + threadIdx.x;
-      v[u] = make_uint2(0, 0);
-      if (j < n) v[u] = get(j);
+// Append the items a visitor yields that satisfy `mem` to (dkey, didx) in any order: one LDS
+// atomic per wave and visit reserves room for the wave's items. Returns the item count
+// (entries past `cap` are dropped). Ends with a barrier. Successive calls alternate between
+// two counters (slot), so a call never resets a counter other threads may still be reading.
+template <class Vis, class Mem>
+__device__ __forceinline__ uint32_t append_members(const Vis& vis, const Mem& mem, uint32_t* dkey, uint32_t* didx,
+                                                   uint32_t cap, int slot, Smem& sm) {
+  uint32_t* counter = &sm.kcount[slot];
+  if (threadIdx.x == 0) *counter = 0;
+  bar();
+  vis([&](uint32_t rk, uint32_t idx) {
+    const bool m = mem(rk, idx);
+    const uint64_t bal = __ballot(m);
+    if (bal) {
+      const int leader = __ffsll((unsigned long long)bal) - 1;
+      uint32_t base = 0;
+      if (lane() == leader) base = atomicAdd(counter, (uint32_t)__popcll(bal));
+      base = (uint32_t)__shfl((int)base, leader, 64);
+      const uint32_t pos = base + mbcnt(bal);
+      if (m && pos < cap) {
+        dkey[pos] = rk;
+        didx[pos] = idx;
+      }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t j = base + u * kThreads + threadIdx.x;
-      if (j < n) f(v[u].x, v[u].y);
-    }
-  }
+  });
+  bar();
+  return *counter;
 }
 
 // ------------------------------------------------------------------ stream kernel
-// Wave 0 only: the highest bin b of the sample histogram with (count in bins >= b) >= thr.
-// Writes res[0] = b, res[1] = count in bins > b, res[2] = count in b.
-__device__ __forceinline__ void search_hist(Smem1& sm, uint32_t thr) {
-  constexpr int kG = kHBins / 64 / 4;   // groups of 4 bins per lane
+// Sample histogram word of bin b: four spare words after every 32 bins, so that lane l's 32
+// bins (wave 0's search reads them as eight 16-byte loads) start 4*l banks apart.
+__device__ __forceinline__ int hword(uint32_t b) { return (int)(b + 4u * (b >> 5)); }
+
+// Wave 0 only: the highest bin b of a sample histogram with (count in bins >= b) >= thr.
+// Writes res[0] = b, res[1] = count in bins > b.
+__device__ __forceinline__ void search_hist(const uint32_t* hist, uint32_t thr, Smem1& sm) {
+  constexpr int kG = 8;   // 8 groups of 4 bins per lane
   const int l = lane();
-  const uint4* h4 = reinterpret_cast<const uint4*>(sm.hist) + kG * l;
+  const uint4* h4 = reinterpret_cast<const uint4*>(hist) + 9 * l;
   uint32_t g[kG];
+  uint4 gv[kG];
   uint32_t lsum = 0;
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
-    const uint4 v = h4[i];
-    g[i] = v.x + v.y + v.z + v.w;
+    gv[i] = h4[i];
+    g[i] = gv[i].x + gv[i].y + gv[i].z + gv[i].w;
     lsum += g[i];
   }
   const uint32_t excl = wave_incl_suffix(lsum) - lsum;
@@ -527,28 +545,19 @@ __device__ __forceinline__ void search_hist(Smem1& sm, uint32_t thr) {
   const int L = bal ? 63 - __clzll((long long)bal) : -1;
   if (l == L) {
     uint32_t acc = excl;
-    int gs = 0;
+    int bin = 0;
     bool done = false;
 #pragma unroll
     for (int i = kG - 1; i >= 0; --i) {
-      const bool hit = !done && (i == 0 || acc + g[i] >= thr);
-      if (hit) { gs = i; done = true; }
-      if (!done) acc += g[i];
-    }
-    const uint4 v = h4[gs];
-    const uint32_t c[4] = {v.x, v.y, v.z, v.w};
-    int j = 0;
-    done = false;
-    uint32_t cj = c[0];
+      const uint32_t c[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
 #pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      const bool hit = !done && (i == 0 || acc + c[i] >= thr);
-      if (hit) { j = i; cj = c[i]; done = true; }
-      if (!done) acc += c[i];
+      for (int j = 3; j >= 0; --j) {
+        if (!done && acc + c[j] >= thr) { bin = 4 * i + j; done = true; }
+        if (!done) acc += c[j];
+      }
     }
-    sm.res[0] = (uint32_t)(kG * 4 * L + 4 * gs + j);
+    sm.res[0] = (uint32_t)(32 * L + bin);
     sm.res[1] = acc;
-    sm.res[2] = cj;
   }
 }
 
@@ -588,7 +597,9 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   const int nfull = n >> 2;
 
   // Issue every load of the chunk before consuming any. Addresses are clamped into the
-  // chunk so all loads are in bounds; elements past the end are masked afterwards.
+  // chunk, so all loads are in bounds and every loaded value is an element of the chunk (a
+  // lane past its wave's range reads a duplicate); duplicates cannot change a maximum or the
+  // NaN flag, and candidate extraction masks them by position.
   uint4 raw[kS1];
   if (aligned && nfull > 0) {
 #pragma unroll
@@ -627,15 +638,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   const RowPlan rp = plan_row(P, MODE, r);
   const int path = rp.path;
   const bool cand = path == kPathCand;
-  if (cand) {
-    uint4* h = reinterpret_cast<uint4*>(sm.hist);
-    for (int i = threadIdx.x; i < kHBins / 4; i += kT1) h[i] = make_uint4(0, 0, 0, 0);
-  }
-  bar();   // LDS only: the loads above stay in flight
 
-  // Work on the fp32 values directly: a key >= threshold-key test is a float >= test against
-  // the threshold's float (ordered keys are a monotone map of fp32, with -0 == +0 in both), so
-  // only the sample and the selected candidates ever need their ordered key.
   auto xval = [&](int s, int e) -> float {
     return __uint_as_float(e == 0 ? raw[s].x : (e == 1 ? raw[s].y : (e == 2 ? raw[s].z : raw[s].w)));
   };
@@ -643,20 +646,31 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
     const int q = q_lo + s * 64 + l;
     return (q < q_hi) ? min(max(n - 4 * q, 0), 4) : 0;
   };
+
   // The candidate threshold comes from a sample, the first kSampleSlots slots of every wave
   // (a quarter of the chunk spread over four segments), so it is known while the rest of
   // the chunk is still arriving. Any threshold is correct (the row kernel certifies); the
   // margin only makes a failed certification rare: the sample's count above the row's k-th
   // key has mean mu = k * ns / V, and the threshold sits mu + 6 sqrt(mu) + 10 keys down.
+  // Work happens on the fp32 values: a key >= threshold-key test is a float >= test against
+  // the threshold's float (ordered keys are a monotone map of fp32, with -0 == +0 in both).
+  // The threshold is located in two levels, each a 2048-bin histogram: the top 11 key bits,
+  // then the next 11 bits of the sample keys inside the chosen bin, so it sits within 2^10
+  // key units (a relative 2^-13 of the value) of the sample's j-th largest key.
   uint32_t thr = kKeyNegInf;   // reported: every valid non-NaN element with key >= thr is emitted
   float thr_f = -INFINITY;
   if (cand) {
+    for (int i = threadIdx.x; i < kHWords / 4; i += kT1) {
+      reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(sm.hist2)[i] = make_uint4(0, 0, 0, 0);
+    }
+    bar();   // LDS only: the loads above stay in flight
 #pragma unroll
     for (int s = 0; s < kSampleSlots; ++s) {
       const int nv = nvalid(s);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (e < nv) atomicAdd(&sm.hist[f2key(xval(s, e)) >> (32 - kHBits)], 1u);
+        if (e < nv) atomicAdd(&sm.hist[hword(f2key(xval(s, e)) >> (32 - kHBits))], 1u);
     }
     uint32_t ns = 0;   // valid sample elements of the workgroup
 #pragma unroll
@@ -669,9 +683,24 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
     const uint32_t jt = (uint32_t)ceilf(mu + 6.0f * sqrtf(mu) + 10.0f);
     if (jt < ns) {
       bar();   // sample histogram complete
-      if (w == 0) search_hist(sm, jt);
+      if (w == 0) search_hist(sm.hist, jt, sm);
       bar();
-      const uint32_t tk = sm.res[0] << (32 - kHBits);
+      const uint32_t b1 = sm.res[0];
+      const uint32_t need2 = jt - sm.res[1];   // >= 1
+#pragma unroll
+      for (int s = 0; s < kSampleSlots; ++s) {
+        const int nv = nvalid(s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = f2key(xval(s, e));   // recomputed: cheaper than 8 live registers
+          if (e < nv && (key >> (32 - kHBits)) == b1)
+            atomicAdd(&sm.hist2[hword((key >> (32 - 2 * kHBits)) & (kHBins - 1))], 1u);
+        }
+      }
+      bar();
+      if (w == 0) search_hist(sm.hist2, need2, sm);
+      bar();
+      const uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - 2 * kHBits));
       if (tk > kKeyNegInf) {
         thr = tk;
         thr_f = key2f(tk);
@@ -679,72 +708,77 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
     }
   }
 
-  // Every slot, as it arrives: chunk statistics (float max, NaN flag) and, on the candidate
-  // path, the ordered append of every value >= thr_f into this wave's LDS region. Ballots
-  // give each selected element its position within the wave's segment ((slot, lane,
-  // element) = id order); the waves' regions concatenate in wave order.
+  // From here on every wave works alone. Each slot as it arrives: the quad maximum (one
+  // max3 chain) feeds the wave maximum and the candidate test; unordered compares of element
+  // pairs feed the NaN flag. A quad whose maximum reaches the threshold is staged (values and
+  // quad index) at its ballot rank, which keeps the staged quads in id order.
   float fmx = -INFINITY;
-  uint32_t nan = 0;
+  bool nan_any = false;
   uint32_t run = 0;
 #pragma unroll
   for (int s = 0; s < kS1; ++s) {
-    const int nv = nvalid(s);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = xval(s, e);
-      const bool valid = e < nv;
-      fmx = valid ? fmaxf(fmx, x) : fmx;
-      nan |= (valid && x != x) ? 1u : 0u;
-    }
+    const float x0 = xval(s, 0), x1 = xval(s, 1), x2 = xval(s, 2), x3 = xval(s, 3);
+    const float mq = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+    fmx = fmaxf(fmx, mq);
+    nan_any |= __builtin_isunordered(x0, x1) | __builtin_isunordered(x2, x3);
     if (cand) {
-      uint64_t mk[4];
-      uint32_t slot_cnt = 0, lane_off = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mk[e] = __ballot(e < nv && xval(s, e) >= thr_f);
-        slot_cnt += (uint32_t)__popcll(mk[e]);
-        lane_off += mbcnt(mk[e]);
-      }
-      uint32_t pos = run + lane_off;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((mk[e] >> l) & 1ull) {
-          if (pos < (uint32_t)kWStage)
-            sm.stage[w][pos] = make_uint2(f2key(xval(s, e)), (uint32_t)(c0 + 4 * (q_lo + s * 64 + l) + e));
-          ++pos;
+      const bool hit = mq >= thr_f;
+      const uint64_t mk = __ballot(hit);
+      if (hit) {
+        const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, run));
+        if (pos < (uint32_t)kQStage) {
+          sm.stage_v[w][pos] = raw[s];
+          sm.stage_q[w][pos] = (uint32_t)(q_lo + s * 64 + l);
         }
       }
-      run += slot_cnt;
+      run += (uint32_t)__popcll(mk);
     }
   }
-  if (cand && l == 0) sm.wave_tot[w] = run;
-  uint32_t kmax = f2key(fmx), kmin_unused = 0u;
-  block_reduce3<kW1>(kmax, kmin_unused, nan, sm.red3);   // its barriers also publish wave_tot
-  const float m_c = key2f(kmax);                          // the chunk maximum
+  const uint32_t kmax = wave_max(f2key(fmx));
+  uint32_t flags = (__ballot(nan_any) != 0ull) ? kFlagNan : 0u;
+  const int64_t seg = ((int64_t)r * P.chunks + c) * kW1 + w;
 
-  uint32_t count = 0, flags = nan ? kFlagNan : 0u, kmax_idx = 0xFFFFFFFFu;
-  uint32_t cmin = 0xFFFFFFFFu;
+  uint32_t count = 0, kmax_idx = 0xFFFFFFFFu;
   float best_s = -INFINITY;
   int32_t best_idx = 0x7FFFFFFF;
 
   if (cand) {
-    uint32_t base = 0, total = 0;
-    bool wave_ovf = false;
+    uint2* out = P.cand + seg * P.cap_w;
+    const uint32_t cap = (uint32_t)P.cap_w;
+    if (run <= (uint32_t)kQStage) {
+      wave_lds_sync();
+      // Extract the staged quads' elements >= thr in id order: a wave scan of the per-lane
+      // counts gives each lane its first position.
+      for (uint32_t i0 = 0; i0 < run; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)l;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        uint32_t q = 0xFFFFFFFFu;
+        if (i < run) {
+          v = sm.stage_v[w][i];
+          q = sm.stage_q[w][i];
+        }
+        const float y[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+        const bool qok = i < run && (int)q < q_hi;
+        bool sel[4];
+        uint32_t cc = 0;
 #pragma unroll
-    for (int ww = 0; ww < kW1; ++ww) {
-      const uint32_t t = sm.wave_tot[ww];
-      base += (ww < w) ? t : 0u;
-      total += t;
-      wave_ovf |= t > (uint32_t)kWStage;
-    }
-    const uint32_t cap = (uint32_t)P.cap_c;
-    uint2* out = P.cand + ((int64_t)r * P.chunks + c) * P.cap_c;
-    if (!wave_ovf) {
-      for (uint32_t i = (uint32_t)l; i < run; i += 64)
-        if (base + i < cap) out[base + i] = sm.stage[w][i];
+        for (int e = 0; e < 4; ++e) {
+          sel[e] = qok && (int)(4 * q) + e < n && y[e] >= thr_f;
+          cc += sel[e] ? 1u : 0u;
+        }
+        const uint32_t incl = wave_incl_scan(cc);
+        uint32_t pos = count + incl - cc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sel[e]) {
+            if (pos < cap) out[pos] = make_uint2(f2key(y[e]), (uint32_t)(c0 + 4 * (int)q + e));
+            ++pos;
+          }
+        }
+        count += wave_total(incl);
+      }
     } else {
-      // a wave's region overflowed: store straight from registers (same positions)
-      uint32_t rr = base;
+      // More hits than the stage holds: the same ordered list, straight from registers.
 #pragma unroll
       for (int s = 0; s < kS1; ++s) {
         const int nv = nvalid(s);
@@ -756,7 +790,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
           slot_cnt += (uint32_t)__popcll(mk[e]);
           lane_off += mbcnt(mk[e]);
         }
-        uint32_t pos = rr + lane_off;
+        uint32_t pos = count + lane_off;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if ((mk[e] >> l) & 1ull) {
@@ -764,25 +798,29 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
             ++pos;
           }
         }
-        rr += slot_cnt;
+        count += slot_cnt;
       }
     }
-    count = min(total, cap);
-    if (total > cap) flags |= kFlagOverflow;
-    cmin = thr;   // every candidate is >= thr: a valid lower bound for the row kernel
+    if (count > cap) {
+      flags |= kFlagOverflow;
+      count = cap;
+    }
   } else if (path == kPathGreedy) {
+    const float m_w = key2f(kmax);
     uint32_t mi = 0xFFFFFFFFu;
 #pragma unroll
     for (int s = 0; s < kS1; ++s) {
       const int nv = nvalid(s);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (e < nv && xval(s, e) == m_c) mi = min(mi, (uint32_t)(c0 + 4 * (q_lo + s * 64 + l) + e));
+        if (e < nv && xval(s, e) == m_w) mi = min(mi, (uint32_t)(c0 + 4 * (q_lo + s * 64 + l) + e));
       }
     }
-    kmax_idx = block_min_u32<kW1>(mi, sm.red);
+    kmax_idx = wave_min(mi);
   } else if (path == kPathFull && MODE == kModeSample) {
-    // Gumbel argmax of the chunk relative to the chunk maximum (one Philox block per quad).
+    // Gumbel argmax of the wave's elements relative to the wave maximum (one Philox block
+    // per quad).
+    const float m_w = key2f(kmax);
     const uint64_t sd = P.seed[r];
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
     float bs = -INFINITY;
@@ -799,97 +837,71 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
         for (int e = 0; e < 4; ++e) {
           if (e < nv) {
             const float g = gumbel_from_uniform(uniform_from_word(words[e]));
-            const float sc = (xval(s, e) - m_c) / rp.t + g;
+            const float sc = (xval(s, e) - m_w) / rp.t + g;
             const int32_t id = (int32_t)(tok0 + e);
             if (sc > bs || (sc == bs && id < bi)) { bs = sc; bi = id; }
           }
         }
       }
     }
-    best_idx = block_argmax<kW1>(bs, bi, sm.reds, sm.redi, &best_s);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float os = __shfl_xor(bs, d, 64);
+      const int32_t oi = __shfl_xor(bi, d, 64);
+      const bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
+      bs = take ? os : bs;
+      bi = take ? oi : bi;
+    }
+    best_s = bs;
+    best_idx = bi;
   }
 
   if (MODE == kModeTopp && P.out_mask) {
     fill_bytes_nt<kT1>(P.out_mask + (int64_t)r * P.V + c0, n, (path == kPathFull) ? (uint8_t)1 : (uint8_t)0);
   }
-  if (threadIdx.x == 0) {
-    ChunkInfo ci;
-    ci.count = count;
-    ci.thr = thr;
-    ci.kmax = kmax;
-    ci.kmin = kKeyNegInf;   // lower bound of every non-NaN key
-    ci.kmax_idx = kmax_idx;
-    ci.flags = flags;
-    ci.best_s = best_s;
-    ci.cmin = cmin;
-    ci.best_idx = best_idx;
-    P.info[(int64_t)r * P.chunks + c] = ci;
+  if (l == 0) {
+    WaveInfo wi;
+    wi.count = count;
+    wi.thr = thr;
+    wi.kmax = kmax;
+    wi.flags = flags;
+    wi.kmax_idx = kmax_idx;
+    wi.best_s = best_s;
+    wi.best_idx = best_idx;
+    wi.pad = 0;
+    P.info[seg] = wi;
   }
 }
 
-// ------------------------------------------------------------------ row-kernel helpers
-constexpr int kMaxSeg = 1024;   // chunks per row the row kernel indexes through LDS offsets
-
-struct SegSrc {
-  // The candidates of a row in id order: one LDS array, or the `chunks` global segments
-  // (chunk c's list at glob + c * cap) addressed through the LDS prefix offsets segoff[].
-  const uint2* lds;
-  const uint2* glob;
-  const uint32_t* segoff;   // chunks + 1 entries: exclusive prefix of the chunk counts
-  uint32_t n;
-  int chunks;
-  int cap;
-  bool in_lds;
-  __device__ __forceinline__ uint2 item(uint32_t j) const {
-    if (in_lds) return lds[j];
-    int lo = 0, hi = chunks;   // largest c with segoff[c] <= j
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (segoff[mid] <= j) lo = mid; else hi = mid;
-    }
-    return glob[(int64_t)lo * cap + (j - segoff[lo])];
-  }
-};
-
-template <class F>
-__device__ __forceinline__ void seg_for_each(const SegSrc& src, F f) {
-  batched_for<8>(src.n, [&](uint32_t j) { return src.item(j); }, f);
-}
-
-template <class Mem, class Out>
-__device__ __forceinline__ void seg_emit_ordered(const SegSrc& src, const Mem& mem, const Out& out, Smem& sm) {
-  uint32_t run = 0;
-  emit_ordered<4>(src.n, [&](uint32_t i, uint32_t& rk, uint32_t& idx) {
-    const uint2 v = src.item(i); rk = v.x; idx = v.y; }, mem, out, run, sm);
-}
-
+// ------------------------------------------------------------------ row kernel
 template <int MODE>
 __device__ __forceinline__ void finish_kset(const Params& P, const RowPlan& rp, int r, uint32_t kmax, uint32_t klo,
-                            uint64_t seed, Smem& sm, int& hb) {
-  // K is in sm.kset (any order; every later step is order-independent).
-  const uint32_t nk = min(sm.kcount, (uint32_t)kFastK);
+                                            uint64_t seed, uint32_t nk, Smem& sm) {
+  // K is in (kkey, kidx)[0, nk), any order: every later step is order-independent.
   const float m = key2f(kmax);
   const float t = rp.t;
   auto kvis = [&](auto f) {
-    for (uint32_t i = threadIdx.x; i < nk; i += kThreads) {
-      const uint2 v = sm.kset[i];
-      f(v.x, v.y);
-    }
+    for (uint32_t i = threadIdx.x; i < nk; i += kRT) f(sm.kkey[i], sm.kidx[i]);
   };
   Sel sp = sel_all();
   uint32_t kept = nk;
   if (rp.p != 1.0f) {
     const int S = 63 - bitlen(nk);
     uint64_t zh = 0, zl = 0;
-    kvis([&](uint32_t rk, uint32_t) {
-      const Mass q = mass_of(weight_of(rk, m, t), S);
+    for (uint32_t i = threadIdx.x; i < nk; i += kRT) {
+      const Mass q = mass_of(weight_of(sm.kkey[i], m, t), S);
+      sm.kmhi[i] = q.hi;
+      sm.kmlo[i] = q.lo;
       zh += q.hi;
       zl += q.lo;
-    });
-    block_sum2_u64(zh, zl, sm.red64);
+    }
+    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also publish kmhi / kmlo
     const double target = (double)rp.p * mass_to_double(zh, zl, S);
-    sp = select_mass(kvis, [&](uint32_t rk) { return weight_of(rk, m, t); }, target, S, nk, kmax,
-                     klo, 0u, (uint32_t)(P.V - 1), sm, hb, kept);
+    auto mvis = [&](auto f) {
+      for (uint32_t i = threadIdx.x; i < nk; i += kRT) f(sm.kkey[i], sm.kidx[i], sm.kmhi[i], sm.kmlo[i]);
+    };
+    sp = select_mass(mvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, nk,
+                     kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -900,24 +912,33 @@ __device__ __forceinline__ void finish_kset(const Params& P, const RowPlan& rp, 
       });
     }
   } else {
+    // Gumbel scores only for the kept set: compact it first (into the candidate arrays, no
+    // longer needed) so that only ceil(|P| / 64) waves draw noise.
+    uint32_t nkept = nk;
+    const uint32_t* gk = sm.kkey;
+    const uint32_t* gi = sm.kidx;
+    if (rp.p != 1.0f) {
+      nkept = append_members(kvis, [&](uint32_t rk, uint32_t idx) { return sel_member(sp, rk, idx); },
+                             sm.ckey, sm.cidx, (uint32_t)kLdsCand, 1, sm);
+      gk = sm.ckey;
+      gi = sm.cidx;
+    }
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
-    kvis([&](uint32_t rk, uint32_t idx) {
-      if (sel_member(sp, rk, idx)) {
-        const float sc = gumbel_score(rk, idx, m, t, (uint32_t)r, k0, k1);
-        if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
-      }
-    });
-    const int32_t tok = block_argmax(bs, bi, sm.reds, sm.redi);
+    for (uint32_t i = threadIdx.x; i < nkept; i += kRT) {
+      const uint32_t idx = gi[i];
+      const float sc = gumbel_score(gk[i], idx, m, t, (uint32_t)r, k0, k1);
+      if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
+    }
+    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
     if (threadIdx.x == 0) P.out_token[r] = tok;
   }
 }
 
-// ------------------------------------------------------------------ row kernel
 template <int MODE>
 __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
-                                           uint32_t kmin, uint64_t seed, Smem& sm, int& hb) {
+                                           uint32_t kmin, uint64_t seed, Smem& sm) {
   // The exact path over the raw row in global memory, one read of the row per pass.
   const float* row = P.x + (int64_t)r * P.stride;
   const uint32_t V = (uint32_t)P.V;
@@ -925,17 +946,17 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   auto rvis = [&](auto f) {
     if (al4) {   // 8 float4 loads in flight per thread per round
       const uint32_t nq = V >> 2;
-      for (uint32_t base = 0; base < nq; base += kThreads * 8) {
+      for (uint32_t base = 0; base < nq; base += kRT * 8) {
         uint4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t q = base + u * kThreads + threadIdx.x;
+          const uint32_t q = base + u * kRT + threadIdx.x;
           v[u] = make_uint4(0, 0, 0, 0);
           if (q < nq) v[u] = reinterpret_cast<const uint4*>(row)[q];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t q = base + u * kThreads + threadIdx.x;
+          const uint32_t q = base + u * kRT + threadIdx.x;
           if (q < nq) {
             f(f2key(__uint_as_float(v[u].x)), 4 * q);
             f(f2key(__uint_as_float(v[u].y)), 4 * q + 1);
@@ -944,22 +965,35 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
           }
         }
       }
-      for (uint32_t i = 4 * nq + threadIdx.x; i < V; i += kThreads) f(f2key(row[i]), i);
+      for (uint32_t i = 4 * nq + threadIdx.x; i < V; i += kRT) f(f2key(row[i]), i);
     } else {
-      batched_for<16>(V, [&](uint32_t j) { return make_uint2(f2key(row[j]), j); }, f);
+      for (uint32_t base = 0; base < V; base += kRT * 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t j = base + u * kRT + threadIdx.x;
+          v[u] = 0;
+          if (j < V) v[u] = f2key(row[j]);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t j = base + u * kRT + threadIdx.x;
+          if (j < V) f(v[u], j);
+        }
+      }
     }
   };
   const uint32_t ke = (uint32_t)rp.k_eff;
   Sel sk = sel_all();
-  if (ke < V) sk = select_topk(rvis, ke, V, kmax, kmin, 0u, V - 1, sm, hb);
+  if (ke < V) sk = select_topk(rvis, ke, V, kmax, kmin, 0u, V - 1, sm);
   if (MODE == kModeTopk) {
     int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
     const uint32_t kmx = (uint32_t)P.k_max;
     uint32_t run = 0;
     emit_ordered<4>(V, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = f2key(row[i]); idx = i; },
-                 [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                 [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
-    for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kThreads) orow[i] = -1;
+                    [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                    [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
+    for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
     return;
   }
   const float m = key2f(kmax);
@@ -979,11 +1013,17 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       zh += q.hi;
       zl += q.lo;
     });
-    block_sum2_u64(zh, zl, sm.red64);
+    block_sum2_u64<kRW>(zh, zl, sm.red64);
     const double target = (double)rp.p * mass_to_double(zh, zl, S);
     const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
-    sp = select_mass(kvis, [&](uint32_t rk) { return weight_of(rk, m, t); }, target, S, ke, kmax,
-                     klo, 0u, V - 1, sm, hb, kept);
+    auto mvis = [&](auto f) {
+      kvis([&](uint32_t rk, uint32_t idx) {
+        const Mass q = mass_of(weight_of(rk, m, t), S);
+        f(rk, idx, q.hi, q.lo);
+      });
+    };
+    sp = select_mass(mvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, ke,
+                     kmax, klo, 0u, V - 1, sm, kept);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -1003,41 +1043,38 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
         if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
       }
     });
-    const int32_t tok = block_argmax(bs, bi, sm.reds, sm.redi);
+    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
     if (threadIdx.x == 0) P.out_token[r] = tok;
   }
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void ts_row_kernel(Params P) {
+__global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   __shared__ Smem sm;
   const int r = (int)blockIdx.x;
-  const ChunkInfo* inf = P.info + (int64_t)r * P.chunks;
-  // Aggregate the chunk summaries (one chunk per thread, then workgroup reductions). Their
-  // loads are issued first; the row parameters and the seed load while they are in flight.
-  uint32_t flags = 0, kmax = 0, kmin = 0xFFFFFFFFu, cmin = 0xFFFFFFFFu, total = 0, thr_max = 0;
-  uint32_t my_count = 0;
-  for (int c = threadIdx.x; c < P.chunks; c += kThreads) {
-    const ChunkInfo ci = inf[c];
-    flags |= ci.flags;
-    kmax = max(kmax, ci.kmax);
-    kmin = min(kmin, ci.kmin);
-    cmin = min(cmin, ci.cmin);
-    thr_max = max(thr_max, ci.thr);
-    total += ci.count;
-    my_count = ci.count;   // used only when chunks <= kThreads
+  const int nseg = P.chunks * kW1;
+  const WaveInfo* inf = P.info + (int64_t)r * nseg;
+  // Aggregate the wave summaries. Their loads are issued first; the row parameters and the
+  // seed load while they are in flight. Counts go to LDS for the segment offsets.
+  uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
+  for (int i = threadIdx.x; i < nseg; i += kRT) {
+    const WaveInfo wi = inf[i];
+    flags |= wi.flags;
+    kmax = max(kmax, wi.kmax);
+    thr_max = max(thr_max, wi.thr);
+    cmin = min(cmin, wi.thr);
+    if (i < kMaxSeg) sm.segoff[i] = wi.count;
   }
   const RowPlan rp = plan_row(P, MODE, r);
   const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
-  int hb = 0;   // histogram buffer of the next radix pass; both start zeroed
-  clear_hist(sm, 0, (int)threadIdx.x, kThreads);
-  clear_hist(sm, 1, (int)threadIdx.x, kThreads);
-  block_reduce3(kmax, kmin, flags, sm.red3);
-  {
-    uint32_t none = 0;
-    block_reduce3(thr_max, cmin, none, sm.red3);
+  // zero the histograms (each select leaves them zero again)
+  reinterpret_cast<uint4*>(sm.hist)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < kDBins / 2; i += kRT) {
+    reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(sm.mlo)[i] = make_uint4(0, 0, 0, 0);
   }
-  total = (uint32_t)block_sum_u64(total, sm.red64);
+  // kmax, thr_max: maxima; cmin: every candidate key is >= the smallest threshold
+  block_reduce4<kRW>(kmax, thr_max, cmin, flags, sm.red);
   const bool nan = (flags & kFlagNan) != 0;
   int st = TS_ROW_OK;
   if (MODE == kModeTopk) {
@@ -1050,10 +1087,10 @@ __global__ __launch_bounds__(kThreads) void ts_row_kernel(Params P) {
 
   if (st != TS_ROW_OK) {
     if (MODE == kModeTopp && rp.path == kPathFull && P.out_mask) {
-      fill_bytes_nt<kThreads>(P.out_mask + (int64_t)r * P.V, P.V, 0);   // chunks had written ones
+      fill_bytes_nt<kRT>(P.out_mask + (int64_t)r * P.V, P.V, 0);   // chunks had written ones
     }
     if (MODE == kModeTopk) {
-      for (int i = threadIdx.x; i < P.k_max; i += kThreads) P.out_idx[(int64_t)r * P.k_max + i] = -1;
+      for (int i = threadIdx.x; i < P.k_max; i += kRT) P.out_idx[(int64_t)r * P.k_max + i] = -1;
     } else if (MODE == kModeTopp) {
       if (threadIdx.x == 0) P.out_kept[r] = 0;
     } else {
@@ -1064,13 +1101,13 @@ __global__ __launch_bounds__(kThreads) void ts_row_kernel(Params P) {
 
   const int path = rp.path;
   if (path == kPathGreedy) {
-    // chunks are in id order: the lowest id holding the row maximum
+    // slices are in id order: the lowest id holding the row maximum
     uint32_t idx = 0xFFFFFFFFu;
-    for (int c = threadIdx.x; c < P.chunks; c += kThreads) {
-      const ChunkInfo ci = inf[c];
-      if (ci.kmax == kmax) idx = min(idx, ci.kmax_idx);
+    for (int i = threadIdx.x; i < nseg; i += kRT) {
+      const WaveInfo wi = inf[i];
+      if (wi.kmax == kmax) idx = min(idx, wi.kmax_idx);
     }
-    idx = block_min_u32(idx, sm.red);
+    idx = block_min_u32<kRW>(idx, sm.red);
     if (MODE == kModeTopp) {
       if (threadIdx.x == 0) {
         P.out_kept[r] = 1;
@@ -1088,103 +1125,103 @@ __global__ __launch_bounds__(kThreads) void ts_row_kernel(Params P) {
       const float m = key2f(kmax);
       float bs = -INFINITY;
       int32_t bi = 0x7FFFFFFF;
-      for (int c = threadIdx.x; c < P.chunks; c += kThreads) {
-        const ChunkInfo ci = inf[c];
-        const float adj = ci.best_s + (key2f(ci.kmax) - m) / rp.t;
-        if (adj > bs || (adj == bs && ci.best_idx < bi)) { bs = adj; bi = ci.best_idx; }
+      for (int i = threadIdx.x; i < nseg; i += kRT) {
+        const WaveInfo wi = inf[i];
+        const float adj = wi.best_s + (key2f(wi.kmax) - m) / rp.t;
+        if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
       }
-      bi = block_argmax(bs, bi, sm.reds, sm.redi);
+      bi = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
       if (threadIdx.x == 0) P.out_token[r] = bi;
     }
     return;
   }
 
-  if (path == kPathCand) {
+  if (path == kPathCand && nseg <= kMaxSeg && !P.force_exact && (flags & kFlagOverflow) == 0) {
     const uint32_t ke = (uint32_t)rp.k_eff;
-    bool ok = ((flags & kFlagOverflow) == 0) && total >= ke && !P.force_exact && P.chunks <= kMaxSeg;
-    if (ok) {
-      // exclusive prefix of the chunk counts: the candidates' flat, id-ordered index space
-      uint32_t tot;
-      const uint32_t off = block_excl_scan(threadIdx.x < (uint32_t)P.chunks ? my_count : 0u, sm.red, tot);
-      if (threadIdx.x < (uint32_t)P.chunks) sm.segoff[threadIdx.x] = off;
-      if (threadIdx.x == 0) sm.segoff[P.chunks] = tot;
+    // exclusive prefix of the slice counts (two consecutive slices per thread): the
+    // candidates' flat, id-ordered index space
+    const int s0 = 2 * (int)threadIdx.x;
+    const uint32_t c0 = s0 < nseg ? sm.segoff[s0] : 0u;
+    const uint32_t c1 = s0 + 1 < nseg ? sm.segoff[s0 + 1] : 0u;
+    uint32_t total;
+    const uint32_t off = block_excl_scan<kRW>(c0 + c1, sm.red, total);   // barrier before writes
+    if (s0 < nseg) sm.segoff[s0] = off;
+    if (s0 + 1 < nseg) sm.segoff[s0 + 1] = off + c0;
+    if (threadIdx.x == 0) sm.segoff[nseg] = total;
+    if (total >= ke && total <= (uint32_t)kLdsCand) {
       bar();
-      SegSrc src;
-      src.glob = P.cand + (int64_t)r * P.chunks * P.cap_c;
-      src.segoff = sm.segoff;
-      src.chunks = P.chunks;
-      src.cap = P.cap_c;
-      src.lds = sm.cand;
-      src.n = total;
-      src.in_lds = false;
-      if (total <= (uint32_t)kLdsCand && !P.leader_global) {
-        // gather the candidates into LDS: each chunk's list is copied by its own group of
-        // threads, up to 8 loads in flight per thread
-        const int G = kThreads / P.chunks;   // >= 1 because chunks <= kMaxSeg
-        const int cg = (int)threadIdx.x / G;
-        const int g = (int)threadIdx.x - cg * G;
-        if (cg < P.chunks) {
-          const uint32_t dst = sm.segoff[cg];
-          const uint32_t nc = sm.segoff[cg + 1] - dst;
-          const uint2* src_c = src.glob + (int64_t)cg * P.cap_c;
-          for (uint32_t j0 = (uint32_t)g; j0 < nc; j0 += (uint32_t)G * 8u) {
-            uint2 v[8];
+      // Gather into LDS: thread t copies the flat range [t*E, t*E + E), locating its first
+      // slice by binary search and walking forward; all loads of a batch are issued first.
+      const uint32_t E = (total + kRT - 1) / kRT;
+      const uint32_t f0 = threadIdx.x * E;
+      const uint32_t f1 = min(f0 + E, total);
+      if (f0 < f1) {
+        int lo = 0, hi = nseg;   // largest s with segoff[s] <= f0
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (sm.segoff[mid] <= f0) lo = mid; else hi = mid;
+        }
+        int s = lo;
+        uint32_t cur = sm.segoff[s], nxt = sm.segoff[s + 1];
+        const uint2* gbase = P.cand + (int64_t)r * nseg * P.cap_w;
+        for (uint32_t fb = f0; fb < f1; fb += 8) {
+          uint2 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const uint32_t j = j0 + (uint32_t)(u * G);
-              v[u] = make_uint2(0, 0);
-              if (j < nc) v[u] = src_c[j];
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t f = fb + u;
+            v[u] = make_uint2(0, 0);
+            if (f < f1) {
+              while (f >= nxt) {
+                ++s;
+                cur = nxt;
+                nxt = sm.segoff[s + 1];
+              }
+              v[u] = gbase[(int64_t)s * P.cap_w + (f - cur)];
             }
+          }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const uint32_t j = j0 + (uint32_t)(u * G);
-              if (j < nc) sm.cand[dst + j] = v[u];
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t f = fb + u;
+            if (f < f1) {
+              sm.ckey[f] = v[u].x;
+              sm.cidx[f] = v[u].y;
             }
           }
         }
-        bar();
-        src.in_lds = true;
       }
-      auto vis = [&](auto f) { seg_for_each(src, f); };
+      bar();
+      auto vis = [&](auto f) {
+        for (uint32_t i = threadIdx.x; i < total; i += kRT) f(sm.ckey[i], sm.cidx[i]);
+      };
       Sel sk = sel_all();
       uint32_t min_sel = cmin;
       if (total > ke) {
-        sk = select_topk(vis, ke, total, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm, hb);
+        sk = select_topk(vis, ke, total, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm);
         min_sel = shl(sk.prefix, sk.lo);
       }
       // Certification: every element of the row with a key >= the smallest selected key
-      // was published by its chunk, so the candidates' top-k is the row's top-k.
+      // was published by its wave, so the candidates' top-k is the row's top-k.
       if (min_sel >= thr_max) {
         if (MODE == kModeTopk) {
           int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
           const uint32_t kmx = (uint32_t)P.k_max;
-          seg_emit_ordered(src, [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                           [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, sm);
-          for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kThreads) orow[i] = -1;
+          uint32_t run = 0;
+          emit_ordered<4>(total, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
+                          [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                          [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
+          for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
           return;
         }
-        if (threadIdx.x == 0) sm.kcount = 0;
-        bar();
-        vis([&](uint32_t rk, uint32_t idx) {
-          // one LDS atomic per wave: the lowest active lane reserves room for the wave
-          const bool mem = sel_member(sk, rk, idx);
-          const uint64_t bal = __ballot(mem);
-          if (bal) {
-            const int leader = __ffsll((unsigned long long)bal) - 1;
-            uint32_t base = 0;
-            if (lane() == leader) base = atomicAdd(&sm.kcount, (uint32_t)__popcll(bal));
-            base = (uint32_t)__shfl((int)base, leader, 64);
-            const uint32_t pos = base + mbcnt(bal);
-            if (mem && pos < (uint32_t)kFastK) sm.kset[pos] = make_uint2(rk, idx);
-          }
-        });
-        bar();
-        finish_kset<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, sm, hb);
+        const uint32_t nk = min(append_members(vis, [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                                               sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
+                                (uint32_t)kFastK);
+        finish_kset<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, nk, sm);
         return;
       }
     }
   }
-  row_stream<MODE>(P, rp, r, kmax, kmin, seed, sm, hb);
+  // the smallest possible key of a non-NaN element
+  row_stream<MODE>(P, rp, r, kmax, kKeyNegInf, seed, sm);
 }
 
 __global__ void ts_fill_kernel(uint32_t* p, size_t n_words) {
@@ -1221,7 +1258,6 @@ int fail(int code, const char* fmt, ...) {
 
 std::atomic<int64_t> g_knob_chunk{0};
 std::atomic<int64_t> g_knob_exact{0};
-std::atomic<int64_t> g_knob_leader_global{0};
 
 struct DevProps {
   bool probed = false;
@@ -1251,12 +1287,14 @@ int check_device(int* dev_out) {
 }
 
 struct Plan {
-  int64_t chunks = 0, chunk_len = 0, cap_c = 0;
+  int64_t chunks = 0, chunk_len = 0, cap_w = 0;
   size_t off_info = 0, off_cand = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Chunking of a row and the workspace layout: per (row, chunk, wave) a WaveInfo, then per
+// (row, chunk, wave) a slice of cap_w candidate slots.
 bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   if (rows < 0 || V < 1 || V > TS_MAX_VOCAB) return false;
   int64_t ce = g_knob_chunk.load();
@@ -1266,14 +1304,16 @@ bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   len = (len + 3) & ~int64_t(3);
   pl.chunk_len = len;
   pl.chunks = (V + len - 1) / len;
-  pl.cap_c = len < kCapMax ? len : kCapMax;
+  const int64_t qw = ((len + 3) / 4 + kW1 - 1) / kW1;   // quads per wave
+  pl.cap_w = 4 * qw < kCapW ? 4 * qw : kCapW;
   const int64_t rr = rows > 0 ? rows : 1;
-  if (rr * pl.chunks > (int64_t)0x7FFFFFFF) return false;
+  if (rr * pl.chunks * kW1 > (int64_t)0x7FFFFFFF) return false;
+  const size_t nseg = (size_t)(rr * pl.chunks * kW1);
   size_t b = 0;
   pl.off_info = b;
-  b += align256((size_t)rr * pl.chunks * sizeof(ChunkInfo));
+  b += align256(nseg * sizeof(WaveInfo));
   pl.off_cand = b;
-  b += align256((size_t)rr * pl.chunks * pl.cap_c * sizeof(uint2));
+  b += align256(nseg * (size_t)pl.cap_w * sizeof(uint2));
   pl.total = b;
   return true;
 }
@@ -1311,23 +1351,22 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.k_max = k_max;
   P.chunks = (int32_t)pl.chunks;
   P.chunk_len = (int32_t)pl.chunk_len;
-  P.cap_c = (int32_t)pl.cap_c;
+  P.cap_w = (int32_t)pl.cap_w;
   P.xcd_map = (pl.chunks > 1 && rows % 8 == 0) ? 1 : 0;
   P.force_exact = (int32_t)g_knob_exact.load();
-  P.leader_global = (int32_t)g_knob_leader_global.load();
   P.out_idx = out_idx;
   P.out_kept = out_kept;
   P.out_mask = out_mask;
   P.out_token = out_token;
   P.status = status;
   char* w = static_cast<char*>(ws);
-  P.info = reinterpret_cast<ChunkInfo*>(w + pl.off_info);
+  P.info = reinterpret_cast<WaveInfo*>(w + pl.off_info);
   P.cand = reinterpret_cast<uint2*>(w + pl.off_cand);
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ts_stream_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "stream kernel launch failed: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(ts_row_kernel<MODE>, dim3((unsigned)rows), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(ts_row_kernel<MODE>, dim3((unsigned)rows), dim3(kRT), 0, s, P);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "row kernel launch failed: %s", hipGetErrorString(e));
   return TS_OK;
@@ -1416,7 +1455,6 @@ int64_t ts_debug_set(int knob, int64_t value) {
       return g_knob_chunk.exchange(value);
     }
     case TS_KNOB_FORCE_EXACT: return g_knob_exact.exchange(value ? 1 : 0);
-    case TS_KNOB_LEADER_GLOBAL: return g_knob_leader_global.exchange(value ? 1 : 0);
     default: return -1;
   }
 }

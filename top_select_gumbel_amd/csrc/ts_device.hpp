@@ -1,15 +1,12 @@
 // ts_device.hpp -- wave64 / workgroup primitives for the gfx950 sampling kernels.
 //
-// Everything here assumes a 1024-thread workgroup (16 waves of 64 lanes) and is called
-// with workgroup-uniform control flow (every thread reaches every barrier).
+// Block-level helpers take the workgroup's wave count NW as a template argument and must be
+// called with workgroup-uniform control flow (every thread reaches every barrier).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace tsd {
-
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ int lane() { return (int)__lane_id(); }
 __device__ __forceinline__ int wave() { return (int)(threadIdx.x >> 6); }
@@ -64,6 +61,34 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += TSD_DPP(v, 0x143, 0xc, 0xf);   // row_bcast:31 into rows 2 and 3
   return v;
 }
+// Maximum over the 64 lanes (every lane gets it): the scan pattern with max in place of add
+// (lanes without a DPP source receive 0, the identity of an unsigned max).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, TSD_DPP(v, 0x111, 0xf, 0xf));
+  v = max(v, TSD_DPP(v, 0x112, 0xf, 0xf));
+  v = max(v, TSD_DPP(v, 0x114, 0xf, 0xf));
+  v = max(v, TSD_DPP(v, 0x118, 0xf, 0xf));
+  v = max(v, TSD_DPP(v, 0x142, 0xa, 0xf));
+  v = max(v, TSD_DPP(v, 0x143, 0xc, 0xf));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return ~wave_max(~v); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= TSD_DPP(v, 0x111, 0xf, 0xf);
+  v |= TSD_DPP(v, 0x112, 0xf, 0xf);
+  v |= TSD_DPP(v, 0x114, 0xf, 0xf);
+  v |= TSD_DPP(v, 0x118, 0xf, 0xf);
+  v |= TSD_DPP(v, 0x142, 0xa, 0xf);
+  v |= TSD_DPP(v, 0x143, 0xc, 0xf);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Orders this wave's LDS accesses: LDS operations of one wave complete in issue order, so a
+// compiler barrier suffices for lanes to read what other lanes of the same wave wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 __device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
   return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
 }
@@ -86,7 +111,7 @@ __device__ __forceinline__ uint64_t wave_incl_suffix64(uint64_t v) {
 // ---------------------------------------------------------------- block reductions
 // `red` is an NW-entry LDS scratch array (NW = waves per workgroup); the function ends with a barrier so it can be
 // reused immediately.
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
@@ -98,7 +123,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   bar();
   return r;
 }
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
@@ -110,7 +135,7 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
   bar();
   return r;
 }
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor(v, d, 64);
@@ -123,7 +148,7 @@ __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
   return r;
 }
 // Workgroup max, min and bitwise-or of three values at once (`red` holds 3 * NW entries).
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ void block_reduce3(uint32_t& mx, uint32_t& mn, uint32_t& orv, uint32_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -145,7 +170,32 @@ __device__ __forceinline__ void block_reduce3(uint32_t& mx, uint32_t& mn, uint32
   }
   bar();
 }
-template <int NW = kWaves>
+// Workgroup max of two values, min of a third and bitwise-or of a fourth at once (`red` holds
+// 4 * NW entries).
+template <int NW>
+__device__ __forceinline__ void block_reduce4(uint32_t& mx1, uint32_t& mx2, uint32_t& mn, uint32_t& orv,
+                                              uint32_t* red) {
+  mx1 = wave_max(mx1);
+  mx2 = wave_max(mx2);
+  mn = wave_min(mn);
+  orv = wave_or(orv);
+  if (lane() == 0) {
+    red[wave()] = mx1;
+    red[NW + wave()] = mx2;
+    red[2 * NW + wave()] = mn;
+    red[3 * NW + wave()] = orv;
+  }
+  bar();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mx1 = max(mx1, red[w]);
+    mx2 = max(mx2, red[NW + w]);
+    mn = min(mn, red[2 * NW + w]);
+    orv |= red[3 * NW + w];
+  }
+  bar();
+}
+template <int NW>
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += (uint64_t)__shfl_xor(v, d, 64);
@@ -158,7 +208,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
   return r;
 }
 // Workgroup sums of two 64-bit values at once (`red` holds 2 * NW entries).
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_t* red) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -180,7 +230,7 @@ __device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_
   bar();
 }
 // Exclusive prefix over the workgroup in thread order; `total` gets the sum of all.
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
   uint32_t incl = wave_incl_scan(v);
   if (lane() == 63) red[wave()] = incl;
@@ -199,7 +249,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
 
 // Argmax over the workgroup of (score, lowest id): every thread gets the winning id and
 // (through best_s) its score.
-template <int NW = kWaves>
+template <int NW>
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
                                                 float* best_s = nullptr) {
 #pragma unroll
