@@ -70,6 +70,8 @@ constexpr int kChunkMax = kT1 * 4 * kS1;            // 8192 logits per chunk
 constexpr int kHBits = 11;                          // sample histogram digit (top key bits)
 constexpr int kHBins = 1 << kHBits;
 constexpr int kHWords = kHBins + kHBins / 8;        // padded: 4 spare words after every 32 bins
+constexpr int kH2Bits = 8;                          // second-level digit inside the chosen bin
+constexpr int kH2Bins = 1 << kH2Bits;
 constexpr int kSampleSlots = 2;                     // slots whose keys form the sample
 constexpr int kQStage = 128;                        // staged quads per wave
 constexpr int kCapW = 512;                          // candidate slots per wave in the workspace
@@ -79,7 +81,9 @@ constexpr int kRW = kRT / 64;
 constexpr int kFastK = 2048;                        // largest k taking the candidate path
 constexpr int kDBits = 11;                          // radix digit of the row selects
 constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel thread
-constexpr int kLdsCand = 6144;                      // candidates the row kernel holds in LDS
+constexpr int kLdsCand = 8192;                      // candidates the row kernel holds in LDS
+constexpr int kVisU = 4;                            // LDS items per thread per visitor round
+constexpr int kGatherB = 12;                        // wave slices per gather batch
 constexpr int kMaxSeg = 2 * kRT;                    // wave slices per row the gather indexes
 static_assert(kDBins == 4 * kRT, "each row-kernel thread owns four histogram bins");
 
@@ -130,17 +134,15 @@ struct RowPlan {
   int32_t bad;
 };
 
-// LDS of the row kernel (about 148 KB; one workgroup per CU)
+// LDS of the row kernel (about 124 KB; one workgroup per CU)
 struct Smem {
   uint32_t ckey[kLdsCand];     // candidates (id order), keys and ids in separate arrays
   uint32_t cidx[kLdsCand];
   alignas(16) uint32_t hist[kDBins];   // count histogram; each thread reads and re-zeroes its own bins
   alignas(16) uint64_t mhi[kDBins];    // mass histogram (fixed-point halves)
   alignas(16) uint64_t mlo[kDBins];
-  uint32_t kkey[kFastK];       // the top-k set K
+  uint32_t kkey[kFastK];       // the kept set P, compacted for the Gumbel draws
   uint32_t kidx[kFastK];
-  uint64_t kmhi[kFastK];       // fixed-point weights of K
-  uint64_t kmlo[kFastK];
   uint32_t segoff[kMaxSeg + 1];
   uint32_t red[4 * kRW];
   uint64_t red64[2 * kRW];
@@ -151,10 +153,10 @@ struct Smem {
   uint32_t kcount[2];
 };
 
-// LDS of the stream kernel (about 28 KB)
+// LDS of the stream kernel (about 20 KB)
 struct Smem1 {
   uint32_t hist[kHWords];      // sample keys by their top 11 bits
-  uint32_t hist2[kHWords];     // sample keys inside the chosen bin, by their next 11 bits
+  uint32_t hist2[kH2Bins];     // sample keys inside the chosen bin, by their next 8 bits
   uint4 stage_v[kW1][kQStage];
   uint32_t stage_q[kW1][kQStage];
   uint32_t res[4];
@@ -295,6 +297,25 @@ __device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t ma
   bar();
 }
 
+// ------------------------------------------------------------------ radix digits
+// The first radix pass over keys in [lo_rk, hi_rk]: the bits above the highest bit where the
+// bounds differ are common (prefix); the digit is the next min(kDBits, lo) bits.
+struct Digit {
+  int lo;
+  int sh;
+  uint32_t dm;
+  uint32_t prefix;
+};
+__device__ __forceinline__ Digit first_digit(uint32_t hi_rk, uint32_t lo_rk) {
+  Digit g;
+  g.lo = (hi_rk == lo_rk) ? 0 : 32 - __clz((int)(hi_rk ^ lo_rk));
+  g.prefix = shr(hi_rk, g.lo);
+  const int d = min(kDBits, g.lo);
+  g.sh = g.lo - d;
+  g.dm = (1u << d) - 1u;
+  return g;
+}
+
 // ------------------------------------------------------------------ exact count select
 // MSB-first radix select of the `need` largest radix keys among the items the visitor
 // yields (vis(f) calls f(rk, idx) for this thread's items; the union over threads must be
@@ -302,15 +323,19 @@ __device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t ma
 // lo_rk differ are common and skipped. A pass stops early when the threshold bin holds
 // exactly the slots still unfilled ([DETK] "Changes": pass skipping). The count histogram
 // is zero on entry and on return.
+// With `prebuilt`, the caller has already counted the first pass (digit first_digit(hi_rk,
+// lo_rk)) into the histogram and passed a barrier; it may do so only when that pass runs
+// (need >= 1 and hi_rk != lo_rk).
 // On return: items with shr(rk, lo) > prefix are selected; eq_take of the tie_cnt items with
 // shr(rk, lo) == prefix must still be taken (lowest ids first).
 template <class Vis>
 __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint32_t n_in_play, uint32_t hi_rk,
                                              uint32_t lo_rk, Smem& sm, uint32_t& prefix, int& lo,
-                                             uint32_t& eq_take, uint32_t& tie_cnt) {
+                                             uint32_t& eq_take, uint32_t& tie_cnt, bool prebuilt = false) {
   lo = (hi_rk == lo_rk) ? 0 : 32 - __clz((int)(hi_rk ^ lo_rk));
   prefix = shr(hi_rk, lo);
   tie_cnt = n_in_play;
+  bool counted = prebuilt;
   while (lo > 0 && need > 0) {
     const int d = min(kDBits, lo);
     const int sh = lo - d;
@@ -318,10 +343,13 @@ __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint
     const uint32_t pre = prefix;
     const int lo_now = lo;
     uint32_t* hist = sm.hist;
-    vis([&](uint32_t rk, uint32_t) {
-      if (shr(rk, lo_now) == pre) atomicAdd(&hist[(rk >> sh) & dm], 1u);
-    });
-    bar();
+    if (!counted) {
+      vis([&](uint32_t rk, uint32_t) {
+        if (shr(rk, lo_now) == pre) atomicAdd(&hist[(rk >> sh) & dm], 1u);
+      });
+      bar();
+    }
+    counted = false;
     search_count(sm, need);
     const uint32_t bin = sm.res[0], above = sm.res[1], cnt = sm.res[2];
     need -= above;
@@ -337,10 +365,11 @@ __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint
 // idx_lo / idx_hi bound the ids of the items.
 template <class Vis>
 __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32_t n_in_play, uint32_t hi_key,
-                                           uint32_t lo_key, uint32_t idx_lo, uint32_t idx_hi, Smem& sm) {
+                                           uint32_t lo_key, uint32_t idx_lo, uint32_t idx_hi, Smem& sm,
+                                           bool prebuilt = false) {
   Sel s;
   uint32_t eq_take, tie_cnt;
-  count_select(vis, need, n_in_play, hi_key, lo_key, sm, s.prefix, s.lo, eq_take, tie_cnt);
+  count_select(vis, need, n_in_play, hi_key, lo_key, sm, s.prefix, s.lo, eq_take, tie_cnt, prebuilt);
   s.cutoff = 0xFFFFFFFFu;
   if (eq_take < tie_cnt) {
     // the eq_take lowest ids among the tied items: select on ~id
@@ -362,19 +391,22 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
 // ------------------------------------------------------------------ mass select (top-p)
 // Smallest prefix of the row ordering whose exact fixed-point mass reaches `target`
 // ([TOPP] "Independent binary64 numerical reference", steps 4-5, with the predicate kept in
-// probability space, [TOPP] "Source basis"). mvis(f) calls f(rk, idx, hi, lo) for this
-// thread's items of K with their fixed-point weight; wmass(rk) returns the weight of a key.
-// Result: Sel of the kept set P (a canonical prefix) and |P| in `kept`. Both histograms are
-// zero on entry and on return.
-template <class MVis, class WMass>
-__device__ __forceinline__ Sel select_mass(const MVis& mvis, const WMass& wmass, double target, int S,
+// probability space, [TOPP] "Source basis"). kvis(f) calls f(rk, idx) for this thread's items
+// of K; wmass(rk) returns the fixed-point weight of a key (computed only for items still in
+// play). Result: Sel of the kept set P (a canonical prefix) and |P| in `kept`. Both histograms
+// are zero on entry and on return. With `prebuilt`, the caller has already accumulated the
+// first pass (digit first_digit(hi_key, lo_key), counts and masses) and passed a barrier; it
+// may do so only when hi_key != lo_key.
+template <class KVis, class WMass>
+__device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, double target, int S,
                                            uint32_t n_in_play, uint32_t hi_key, uint32_t lo_key,
-                                           uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept) {
+                                           uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept,
+                                           bool prebuilt = false) {
   int lo = (hi_key == lo_key) ? 0 : 32 - __clz((int)(hi_key ^ lo_key));
   uint32_t prefix = shr(hi_key, lo);
   uint32_t n_above = 0, tie_cnt = n_in_play;
   uint64_t ma_hi = 0, ma_lo = 0, bin_hi = 0, bin_lo = 0;
-  bool single = false, ran = false;
+  bool single = false, ran = false, counted = prebuilt;
   while (lo > 0) {
     const int d = min(kDBits, lo);
     const int sh = lo - d;
@@ -382,15 +414,19 @@ __device__ __forceinline__ Sel select_mass(const MVis& mvis, const WMass& wmass,
     const uint32_t pre = prefix;
     const int lo_now = lo;
     ran = true;
-    mvis([&](uint32_t rk, uint32_t, uint64_t hi, uint64_t lo_m) {
-      if (shr(rk, lo_now) == pre) {
-        const uint32_t b = (rk >> sh) & dm;
-        atomicAdd(&sm.hist[b], 1u);
-        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)hi);
-        atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)lo_m);
-      }
-    });
-    bar();
+    if (!counted) {
+      kvis([&](uint32_t rk, uint32_t) {
+        if (shr(rk, lo_now) == pre) {
+          const uint32_t b = (rk >> sh) & dm;
+          const Mass q = wmass(rk);
+          atomicAdd(&sm.hist[b], 1u);
+          atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q.hi);
+          atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
+        }
+      });
+      bar();
+    }
+    counted = false;
     search_mass(sm, target, ma_hi, ma_lo, S);
     const uint32_t bin = sm.res[0];
     n_above += sm.res[1];
@@ -430,7 +466,7 @@ __device__ __forceinline__ Sel select_mass(const MVis& mvis, const WMass& wmass,
     const uint32_t pre = prefix;
     const int lo_ = lo;
     auto tvis = [&](auto f) {
-      mvis([&](uint32_t rk, uint32_t idx, uint64_t, uint64_t) {
+      kvis([&](uint32_t rk, uint32_t idx) {
         if (shr(rk, lo_) == pre) f(~idx, idx);
       });
     };
@@ -491,31 +527,73 @@ __device__ __forceinline__ void emit_ordered(uint32_t n, const Get& get, const M
   }
 }
 
-// Append the items a visitor yields that satisfy `mem` to (dkey, didx) in any order: one LDS
-// atomic per wave and visit reserves room for the wave's items. Returns the item count
-// (entries past `cap` are dropped). Ends with a barrier. Successive calls alternate between
-// two counters (slot), so a call never resets a counter other threads may still be reading.
-template <class Vis, class Mem>
-__device__ __forceinline__ uint32_t append_members(const Vis& vis, const Mem& mem, uint32_t* dkey, uint32_t* didx,
+// Visit the items [0, n) of an LDS (key, id) array pair: kVisU per thread per round, all LDS
+// reads of a round issued before any item is used. f(rk, idx) is called for each item.
+template <class F>
+__device__ __forceinline__ void lds_for(const uint32_t* ka, const uint32_t* ia, uint32_t n, F f) {
+  for (uint32_t base = threadIdx.x; base < n; base += kRT * kVisU) {
+    uint32_t k[kVisU], x[kVisU];
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      const uint32_t i = min(base + u * kRT, n - 1);   // clamped: in bounds, result unused past n
+      k[u] = ka[i];
+      x[u] = ia[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      if (base + u * kRT < n) f(k[u], x[u]);
+    }
+  }
+}
+
+// Append the items of [0, n) of (ka, ia) that satisfy `mem` to (dkey, didx), in any order:
+// per round, a wave scan of the per-lane counts and one LDS atomic per wave reserve room.
+// Returns the count (entries past `cap` are dropped). Ends with a barrier. Successive calls
+// alternate between two counters (slot), so a call never resets a counter that other
+// threads may still be reading.
+template <class Mem>
+__device__ __forceinline__ uint32_t append_members(const uint32_t* ka, const uint32_t* ia, uint32_t n,
+                                                   const Mem& mem, uint32_t* dkey, uint32_t* didx,
                                                    uint32_t cap, int slot, Smem& sm) {
   uint32_t* counter = &sm.kcount[slot];
   if (threadIdx.x == 0) *counter = 0;
   bar();
-  vis([&](uint32_t rk, uint32_t idx) {
-    const bool m = mem(rk, idx);
-    const uint64_t bal = __ballot(m);
-    if (bal) {
-      const int leader = __ffsll((unsigned long long)bal) - 1;
-      uint32_t base = 0;
-      if (lane() == leader) base = atomicAdd(counter, (uint32_t)__popcll(bal));
-      base = (uint32_t)__shfl((int)base, leader, 64);
-      const uint32_t pos = base + mbcnt(bal);
-      if (m && pos < cap) {
-        dkey[pos] = rk;
-        didx[pos] = idx;
+  for (uint32_t base = threadIdx.x - (uint32_t)lane(); base < n; base += kRT * kVisU) {
+    // wave-uniform loop: base is the wave's first item of the round
+    uint32_t k[kVisU], x[kVisU];
+    bool m[kVisU];
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      const uint32_t i = min(base + (uint32_t)lane() + u * kRT, n - 1);
+      k[u] = ka[i];
+      x[u] = ia[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      const uint32_t i = base + (uint32_t)lane() + u * kRT;
+      m[u] = i < n && mem(k[u], x[u]);
+      c += m[u] ? 1u : 0u;
+    }
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t tot = wave_total(incl);
+    uint32_t wbase = 0;
+    if (tot) {
+      if (lane() == 63) wbase = atomicAdd(counter, tot);
+      wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63);
+    }
+    uint32_t pos = wbase + incl - c;
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      if (m[u]) {
+        if (pos < cap) {
+          dkey[pos] = k[u];
+          didx[pos] = x[u];
+        }
+        ++pos;
       }
     }
-  });
+  }
   bar();
   return *counter;
 }
@@ -558,6 +636,26 @@ __device__ __forceinline__ void search_hist(const uint32_t* hist, uint32_t thr, 
     }
     sm.res[0] = (uint32_t)(32 * L + bin);
     sm.res[1] = acc;
+  }
+}
+
+// Wave 0 only: the same search over the 256-bin second level (four bins per lane).
+__device__ __forceinline__ void search_hist2(const uint32_t* hist, uint32_t thr, Smem1& sm) {
+  const int l = lane();
+  const uint4 v = reinterpret_cast<const uint4*>(hist)[l];
+  const uint32_t lsum = v.x + v.y + v.z + v.w;
+  const uint32_t excl = wave_incl_suffix(lsum) - lsum;
+  const uint64_t bal = __ballot(excl + lsum >= thr);
+  const int L = bal ? 63 - __clzll((long long)bal) : -1;
+  if (l == L) {
+    const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+    uint32_t acc = excl;
+    int j = 3;
+    for (; j > 0; --j) {
+      if (acc + c[j] >= thr) break;
+      acc += c[j];
+    }
+    sm.res[0] = (uint32_t)(4 * L + j);
   }
 }
 
@@ -654,16 +752,14 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   // key has mean mu = k * ns / V, and the threshold sits mu + 6 sqrt(mu) + 10 keys down.
   // Work happens on the fp32 values: a key >= threshold-key test is a float >= test against
   // the threshold's float (ordered keys are a monotone map of fp32, with -0 == +0 in both).
-  // The threshold is located in two levels, each a 2048-bin histogram: the top 11 key bits,
-  // then the next 11 bits of the sample keys inside the chosen bin, so it sits within 2^10
-  // key units (a relative 2^-13 of the value) of the sample's j-th largest key.
+  // The threshold is located in two levels: a 2048-bin histogram of the top 11 key bits, then
+  // a 256-bin one of the next 8 bits of the sample keys inside the chosen bin, so it sits
+  // within 2^13 key units (a relative 2^-10 of the value) of the sample's j-th largest key.
   uint32_t thr = kKeyNegInf;   // reported: every valid non-NaN element with key >= thr is emitted
   float thr_f = -INFINITY;
   if (cand) {
-    for (int i = threadIdx.x; i < kHWords / 4; i += kT1) {
-      reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
-      reinterpret_cast<uint4*>(sm.hist2)[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = threadIdx.x; i < kHWords / 4; i += kT1) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+    if (threadIdx.x < kH2Bins) sm.hist2[threadIdx.x] = 0u;
     bar();   // LDS only: the loads above stay in flight
 #pragma unroll
     for (int s = 0; s < kSampleSlots; ++s) {
@@ -694,13 +790,13 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = f2key(xval(s, e));   // recomputed: cheaper than 8 live registers
           if (e < nv && (key >> (32 - kHBits)) == b1)
-            atomicAdd(&sm.hist2[hword((key >> (32 - 2 * kHBits)) & (kHBins - 1))], 1u);
+            atomicAdd(&sm.hist2[(key >> (32 - kHBits - kH2Bits)) & (kH2Bins - 1)], 1u);
         }
       }
       bar();
-      if (w == 0) search_hist(sm.hist2, need2, sm);
+      if (w == 0) search_hist2(sm.hist2, need2, sm);
       bar();
-      const uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - 2 * kHBits));
+      const uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - kHBits - kH2Bits));
       if (tk > kKeyNegInf) {
         thr = tk;
         thr_f = key2f(tk);
@@ -844,16 +940,9 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
         }
       }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float os = __shfl_xor(bs, d, 64);
-      const int32_t oi = __shfl_xor(bi, d, 64);
-      const bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
-      bs = take ? os : bs;
-      bi = take ? oi : bi;
-    }
-    best_s = bs;
-    best_idx = bi;
+    wave_argmax(bs, bi);
+    best_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bs), 63));
+    best_idx = __builtin_amdgcn_readlane(bi, 63);
   }
 
   if (MODE == kModeTopp && P.out_mask) {
@@ -875,33 +964,41 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
 
 // ------------------------------------------------------------------ row kernel
 template <int MODE>
-__device__ __forceinline__ void finish_kset(const Params& P, const RowPlan& rp, int r, uint32_t kmax, uint32_t klo,
-                                            uint64_t seed, uint32_t nk, Smem& sm) {
-  // K is in (kkey, kidx)[0, nk), any order: every later step is order-independent.
+__device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, int r, uint32_t kmax, uint32_t klo,
+                                            uint64_t seed, uint32_t total, const Sel& sk, Smem& sm) {
+  // K = the candidates selected by sk, compacted into (kkey, kidx) in any order: every step
+  // below is order-independent.
+  const uint32_t nk = min(append_members(sm.ckey, sm.cidx, total,
+                                         [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                                         sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
+                          (uint32_t)kFastK);
   const float m = key2f(kmax);
   const float t = rp.t;
-  auto kvis = [&](auto f) {
-    for (uint32_t i = threadIdx.x; i < nk; i += kRT) f(sm.kkey[i], sm.kidx[i]);
-  };
+  auto kvis = [&](auto f) { lds_for(sm.kkey, sm.kidx, nk, f); };
   Sel sp = sel_all();
   uint32_t kept = nk;
   if (rp.p != 1.0f) {
+    // One visit of K computes every weight once: Z, and the counts and masses of the mass
+    // select's first pass.
     const int S = 63 - bitlen(nk);
+    auto wmass = [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); };
+    const Digit g = first_digit(kmax, klo);
+    const bool pre = g.lo > 0;
     uint64_t zh = 0, zl = 0;
-    for (uint32_t i = threadIdx.x; i < nk; i += kRT) {
-      const Mass q = mass_of(weight_of(sm.kkey[i], m, t), S);
-      sm.kmhi[i] = q.hi;
-      sm.kmlo[i] = q.lo;
+    kvis([&](uint32_t rk, uint32_t) {
+      const Mass q = wmass(rk);
       zh += q.hi;
       zl += q.lo;
-    }
-    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also publish kmhi / kmlo
+      if (pre) {
+        const uint32_t b = (rk >> g.sh) & g.dm;
+        atomicAdd(&sm.hist[b], 1u);
+        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q.hi);
+        atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
+      }
+    });
+    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics
     const double target = (double)rp.p * mass_to_double(zh, zl, S);
-    auto mvis = [&](auto f) {
-      for (uint32_t i = threadIdx.x; i < nk; i += kRT) f(sm.kkey[i], sm.kidx[i], sm.kmhi[i], sm.kmlo[i]);
-    };
-    sp = select_mass(mvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, nk,
-                     kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept);
+    sp = select_mass(kvis, wmass, target, S, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -912,14 +1009,15 @@ __device__ __forceinline__ void finish_kset(const Params& P, const RowPlan& rp, 
       });
     }
   } else {
-    // Gumbel scores only for the kept set: compact it first (into the candidate arrays, no
-    // longer needed) so that only ceil(|P| / 64) waves draw noise.
+    // Gumbel scores only for the kept set: compact it (into the candidate arrays, no longer
+    // needed) so that only ceil(|P| / 64) waves draw noise.
     uint32_t nkept = nk;
     const uint32_t* gk = sm.kkey;
     const uint32_t* gi = sm.kidx;
     if (rp.p != 1.0f) {
-      nkept = append_members(kvis, [&](uint32_t rk, uint32_t idx) { return sel_member(sp, rk, idx); },
-                             sm.ckey, sm.cidx, (uint32_t)kLdsCand, 1, sm);
+      nkept = min(append_members(sm.kkey, sm.kidx, nk, [&](uint32_t rk, uint32_t idx) { return sel_member(sp, rk, idx); },
+                                 sm.ckey, sm.cidx, (uint32_t)kLdsCand, 1, sm),
+                  (uint32_t)kLdsCand);
       gk = sm.ckey;
       gi = sm.cidx;
     }
@@ -1016,13 +1114,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
     block_sum2_u64<kRW>(zh, zl, sm.red64);
     const double target = (double)rp.p * mass_to_double(zh, zl, S);
     const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
-    auto mvis = [&](auto f) {
-      kvis([&](uint32_t rk, uint32_t idx) {
-        const Mass q = mass_of(weight_of(rk, m, t), S);
-        f(rk, idx, q.hi, q.lo);
-      });
-    };
-    sp = select_mass(mvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, ke,
+    sp = select_mass(kvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, ke,
                      kmax, klo, 0u, V - 1, sm, kept);
   }
   if (MODE == kModeTopp) {
@@ -1055,7 +1147,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
   // Aggregate the wave summaries. Their loads are issued first; the row parameters and the
-  // seed load while they are in flight. Counts go to LDS for the segment offsets.
+  // seed load while they are in flight. Counts go to LDS for the slice offsets.
   uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
   for (int i = threadIdx.x; i < nseg; i += kRT) {
     const WaveInfo wi = inf[i];
@@ -1150,53 +1242,55 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     if (threadIdx.x == 0) sm.segoff[nseg] = total;
     if (total >= ke && total <= (uint32_t)kLdsCand) {
       bar();
-      // Gather into LDS: thread t copies the flat range [t*E, t*E + E), locating its first
-      // slice by binary search and walking forward; all loads of a batch are issued first.
-      const uint32_t E = (total + kRT - 1) / kRT;
-      const uint32_t f0 = threadIdx.x * E;
-      const uint32_t f1 = min(f0 + E, total);
-      if (f0 < f1) {
-        int lo = 0, hi = nseg;   // largest s with segoff[s] <= f0
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sm.segoff[mid] <= f0) lo = mid; else hi = mid;
-        }
-        int s = lo;
-        uint32_t cur = sm.segoff[s], nxt = sm.segoff[s + 1];
-        const uint2* gbase = P.cand + (int64_t)r * nseg * P.cap_w;
-        for (uint32_t fb = f0; fb < f1; fb += 8) {
-          uint2 v[8];
+      // The top-k select's first pass is counted while the candidates are written to LDS:
+      // every candidate key lies in [cmin, kmax], so its digit needs no prefix test.
+      const Digit g0 = first_digit(kmax, cmin);
+      const bool pre = total > ke && g0.lo > 0;
+      auto put = [&](uint32_t f, uint2 v) {
+        sm.ckey[f] = v.x;
+        sm.cidx[f] = v.y;
+        if (pre) atomicAdd(&sm.hist[(v.x >> g0.sh) & g0.dm], 1u);
+      };
+      {
+        // Wave w copies slices w, w + kRW, ...: lane l takes slot l of each (coalesced). Per
+        // batch of kGatherB slices the offsets are read first, then every load is issued,
+        // then the candidates are written; slices holding more than 64 finish afterwards.
+        for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
+          uint32_t o[kGatherB], cnt[kGatherB];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const uint32_t f = fb + u;
-            v[u] = make_uint2(0, 0);
-            if (f < f1) {
-              while (f >= nxt) {
-                ++s;
-                cur = nxt;
-                nxt = sm.segoff[s + 1];
-              }
-              v[u] = gbase[(int64_t)s * P.cap_w + (f - cur)];
-            }
+          for (int u = 0; u < kGatherB; ++u) {
+            const int sl = min(sb + u * kRW, nseg);   // slice nseg has no candidates
+            o[u] = sm.segoff[sl];
+            cnt[u] = sm.segoff[min(sl + 1, nseg)] - o[u];
           }
+          const uint2* gs = P.cand + ((int64_t)r * nseg + sb) * P.cap_w;
+          const uint32_t j = (uint32_t)lane();
+          uint2 v[kGatherB];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const uint32_t f = fb + u;
-            if (f < f1) {
-              sm.ckey[f] = v[u].x;
-              sm.cidx[f] = v[u].y;
+          for (int u = 0; u < kGatherB; ++u) {
+            v[u] = make_uint2(0, 0);
+            if (j < cnt[u]) v[u] = gs[(int64_t)u * kRW * P.cap_w + j];
+          }
+          bool more = false;
+#pragma unroll
+          for (int u = 0; u < kGatherB; ++u) {
+            if (j < cnt[u]) put(o[u] + j, v[u]);
+            more |= cnt[u] > 64u;
+          }
+          if (more) {   // wave-uniform: some slice of the batch holds more than 64 candidates
+#pragma unroll
+            for (int u = 0; u < kGatherB; ++u) {
+              for (uint32_t jj = 64u + j; jj < cnt[u]; jj += 64u) put(o[u] + jj, gs[(int64_t)u * kRW * P.cap_w + jj]);
             }
           }
         }
       }
       bar();
-      auto vis = [&](auto f) {
-        for (uint32_t i = threadIdx.x; i < total; i += kRT) f(sm.ckey[i], sm.cidx[i]);
-      };
+      auto vis = [&](auto f) { lds_for(sm.ckey, sm.cidx, total, f); };
       Sel sk = sel_all();
       uint32_t min_sel = cmin;
       if (total > ke) {
-        sk = select_topk(vis, ke, total, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm);
+        sk = select_topk(vis, ke, total, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm, pre);
         min_sel = shl(sk.prefix, sk.lo);
       }
       // Certification: every element of the row with a key >= the smallest selected key
@@ -1212,10 +1306,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
           return;
         }
-        const uint32_t nk = min(append_members(vis, [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                                               sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
-                                (uint32_t)kFastK);
-        finish_kset<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, nk, sm);
+        finish_cand<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, total, sk, sm);
         return;
       }
     }

@@ -1,7 +1,8 @@
 // ts_device.hpp -- wave64 / workgroup primitives for the gfx950 sampling kernels.
 //
 // Block-level helpers take the workgroup's wave count NW as a template argument and must be
-// called with workgroup-uniform control flow (every thread reaches every barrier).
+// called with workgroup-uniform control flow (every thread reaches every barrier). Wave-level
+// reductions and scans use DPP lane moves (a few cycles each) rather than LDS permutes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -20,6 +21,14 @@ __device__ __forceinline__ void bar() {
 }
 // Barrier that also orders global memory between the threads of the workgroup.
 __device__ __forceinline__ void bar_all() { __syncthreads(); }
+
+// Orders this wave's LDS accesses: LDS operations of one wave complete in issue order, so a
+// compiler barrier suffices for lanes to read what other lanes of the same wave wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : (x >> s); }
 __device__ __forceinline__ uint32_t shl(uint32_t x, int s) { return s >= 32 ? 0u : (x << s); }
@@ -45,52 +54,49 @@ __device__ __forceinline__ float key2f(uint32_t k) {
 constexpr uint32_t kKeyPosInf = 0xFF800000u;   // f2key(+inf)
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // f2key(-inf)
 
-// ---------------------------------------------------------------- wave scans
-// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips): Hillis-Steele
-// shifts of 1, 2, 4, 8 inside each 16-lane row, then row 0's total is broadcast into row 1
-// and row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31).
-// Lanes whose DPP source is outside the row or masked receive 0.
-#define TSD_DPP(v, ctrl, rmask, bmask) \
-  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rmask), (bmask), false))
+// ---------------------------------------------------------------- wave scans / reductions
+// The lane pattern of an inclusive scan over 64 lanes: Hillis-Steele shifts of 1, 2, 4, 8
+// inside each 16-lane row, then row 0's last lane is broadcast into row 1 and row 2's into
+// row 3 (row_bcast:15), then row 1's last lane into rows 2-3 (row_bcast:31). A lane whose
+// source lies outside its row (or whose row is masked) receives the `identity` operand of
+// the combining operation. Lane 63 ends with the combination of all lanes.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, RMASK, 0xf, false);
+}
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = dpp32<CTRL, RMASK>((uint32_t)v, 0u);
+  const uint32_t hi = dpp32<CTRL, RMASK>((uint32_t)(v >> 32), 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += TSD_DPP(v, 0x111, 0xf, 0xf);   // row_shr:1
-  v += TSD_DPP(v, 0x112, 0xf, 0xf);   // row_shr:2
-  v += TSD_DPP(v, 0x114, 0xf, 0xf);   // row_shr:4
-  v += TSD_DPP(v, 0x118, 0xf, 0xf);   // row_shr:8
-  v += TSD_DPP(v, 0x142, 0xa, 0xf);   // row_bcast:15 into rows 1 and 3
-  v += TSD_DPP(v, 0x143, 0xc, 0xf);   // row_bcast:31 into rows 2 and 3
+  v += dpp32<0x111, 0xf>(v, 0u);   // row_shr:1
+  v += dpp32<0x112, 0xf>(v, 0u);   // row_shr:2
+  v += dpp32<0x114, 0xf>(v, 0u);   // row_shr:4
+  v += dpp32<0x118, 0xf>(v, 0u);   // row_shr:8
+  v += dpp32<0x142, 0xa>(v, 0u);   // row_bcast:15 into rows 1 and 3
+  v += dpp32<0x143, 0xc>(v, 0u);   // row_bcast:31 into rows 2 and 3
   return v;
 }
-// Maximum over the 64 lanes (every lane gets it): the scan pattern with max in place of add
-// (lanes without a DPP source receive 0, the identity of an unsigned max).
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, TSD_DPP(v, 0x111, 0xf, 0xf));
-  v = max(v, TSD_DPP(v, 0x112, 0xf, 0xf));
-  v = max(v, TSD_DPP(v, 0x114, 0xf, 0xf));
-  v = max(v, TSD_DPP(v, 0x118, 0xf, 0xf));
-  v = max(v, TSD_DPP(v, 0x142, 0xa, 0xf));
-  v = max(v, TSD_DPP(v, 0x143, 0xc, 0xf));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return ~wave_max(~v); }
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  v |= TSD_DPP(v, 0x111, 0xf, 0xf);
-  v |= TSD_DPP(v, 0x112, 0xf, 0xf);
-  v |= TSD_DPP(v, 0x114, 0xf, 0xf);
-  v |= TSD_DPP(v, 0x118, 0xf, 0xf);
-  v |= TSD_DPP(v, 0x142, 0xa, 0xf);
-  v |= TSD_DPP(v, 0x143, 0xc, 0xf);
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-// Orders this wave's LDS accesses: LDS operations of one wave complete in issue order, so a
-// compiler barrier suffices for lanes to read what other lanes of the same wave wrote.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// 64-bit values: the same moves on both halves, added with carry.
+__device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t v) {
+  v += dpp64<0x111, 0xf>(v);
+  v += dpp64<0x112, 0xf>(v);
+  v += dpp64<0x114, 0xf>(v);
+  v += dpp64<0x118, 0xf>(v);
+  v += dpp64<0x142, 0xa>(v);
+  v += dpp64<0x143, 0xc>(v);
+  return v;
 }
 __device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
   return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 // Inclusive suffix sums: lane l gets the sum over lanes >= l.
 __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v) {
@@ -98,23 +104,54 @@ __device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v) {
   return wave_total(incl) - incl + v;
 }
 __device__ __forceinline__ uint64_t wave_incl_suffix64(uint64_t v) {
-  // two 32-bit DPP scans with the carry of the low half folded into the high half
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t lo_hi16 = lo >> 16, lo_lo16 = lo & 0xFFFFu;
-  // sums of 64 values below 2^16 stay below 2^22, so the split halves cannot overflow
-  const uint32_t s_lo16 = wave_incl_suffix(lo_lo16);
-  const uint32_t s_hi16 = wave_incl_suffix(lo_hi16);
-  const uint32_t s_hi = wave_incl_suffix(hi);
-  return ((uint64_t)s_hi << 32) + ((uint64_t)s_hi16 << 16) + (uint64_t)s_lo16;
+  const uint64_t incl = wave_incl_scan64(v);
+  return readlane64(incl, 63) - incl + v;
+}
+// Maximum / minimum / or over the 64 lanes (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp32<0x111, 0xf>(v, 0u));
+  v = max(v, dpp32<0x112, 0xf>(v, 0u));
+  v = max(v, dpp32<0x114, 0xf>(v, 0u));
+  v = max(v, dpp32<0x118, 0xf>(v, 0u));
+  v = max(v, dpp32<0x142, 0xa>(v, 0u));
+  v = max(v, dpp32<0x143, 0xc>(v, 0u));
+  return wave_total(v);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return ~wave_max(~v); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp32<0x111, 0xf>(v, 0u);
+  v |= dpp32<0x112, 0xf>(v, 0u);
+  v |= dpp32<0x114, 0xf>(v, 0u);
+  v |= dpp32<0x118, 0xf>(v, 0u);
+  v |= dpp32<0x142, 0xa>(v, 0u);
+  v |= dpp32<0x143, 0xc>(v, 0u);
+  return wave_total(v);
+}
+// One step of the argmax combine of (score, lowest id); a lane without a source sees
+// (-inf, INT_MAX), which never wins.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ void argmax_step(float& s, int32_t& id) {
+  const float os = __uint_as_float(dpp32<CTRL, RMASK>(__float_as_uint(s), __float_as_uint(-INFINITY)));
+  const int32_t oi = (int32_t)dpp32<CTRL, RMASK>((uint32_t)id, 0x7FFFFFFFu);
+  const bool take = (os > s) || (os == s && (uint32_t)oi < (uint32_t)id);
+  s = take ? os : s;
+  id = take ? oi : id;
+}
+// Argmax of (score, lowest id) over the wave; the result is in lane 63.
+__device__ __forceinline__ void wave_argmax(float& s, int32_t& id) {
+  argmax_step<0x111, 0xf>(s, id);
+  argmax_step<0x112, 0xf>(s, id);
+  argmax_step<0x114, 0xf>(s, id);
+  argmax_step<0x118, 0xf>(s, id);
+  argmax_step<0x142, 0xa>(s, id);
+  argmax_step<0x143, 0xc>(s, id);
 }
 
 // ---------------------------------------------------------------- block reductions
-// `red` is an NW-entry LDS scratch array (NW = waves per workgroup); the function ends with a barrier so it can be
-// reused immediately.
-template <int NW>
+// `red` is LDS scratch (sizes below); each helper ends with a barrier so it can be reused.
+template <int NW>   // red: NW entries
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
+  v = wave_max(v);
   if (lane() == 0) red[wave()] = v;
   bar();
   uint32_t r = red[0];
@@ -123,55 +160,11 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   bar();
   return r;
 }
-template <int NW>
+template <int NW>   // red: NW entries
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
-  if (lane() == 0) red[wave()] = v;
-  bar();
-  uint32_t r = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) r = min(r, red[w]);
-  bar();
-  return r;
+  return ~block_max_u32<NW>(~v, red);
 }
-template <int NW>
-__device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor(v, d, 64);
-  if (lane() == 0) red[wave()] = v;
-  bar();
-  uint32_t r = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) r |= red[w];
-  bar();
-  return r;
-}
-// Workgroup max, min and bitwise-or of three values at once (`red` holds 3 * NW entries).
-template <int NW>
-__device__ __forceinline__ void block_reduce3(uint32_t& mx, uint32_t& mn, uint32_t& orv, uint32_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mx = max(mx, (uint32_t)__shfl_xor(mx, d, 64));
-    mn = min(mn, (uint32_t)__shfl_xor(mn, d, 64));
-    orv |= (uint32_t)__shfl_xor(orv, d, 64);
-  }
-  if (lane() == 0) {
-    red[wave()] = mx;
-    red[NW + wave()] = mn;
-    red[2 * NW + wave()] = orv;
-  }
-  bar();
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    mx = max(mx, red[w]);
-    mn = min(mn, red[NW + w]);
-    orv |= red[2 * NW + w];
-  }
-  bar();
-}
-// Workgroup max of two values, min of a third and bitwise-or of a fourth at once (`red` holds
-// 4 * NW entries).
+// Max of two values, min of a third and bitwise-or of a fourth at once (red: 4 * NW).
 template <int NW>
 __device__ __forceinline__ void block_reduce4(uint32_t& mx1, uint32_t& mx2, uint32_t& mn, uint32_t& orv,
                                               uint32_t* red) {
@@ -195,27 +188,12 @@ __device__ __forceinline__ void block_reduce4(uint32_t& mx1, uint32_t& mx2, uint
   }
   bar();
 }
-template <int NW>
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += (uint64_t)__shfl_xor(v, d, 64);
-  if (lane() == 0) red[wave()] = v;
-  bar();
-  uint64_t r = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) r += red[w];
-  bar();
-  return r;
-}
-// Workgroup sums of two 64-bit values at once (`red` holds 2 * NW entries).
+// Sums of two 64-bit values at once (red: 2 * NW).
 template <int NW>
 __device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_t* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    a += (uint64_t)__shfl_xor(a, d, 64);
-    b += (uint64_t)__shfl_xor(b, d, 64);
-  }
-  if (lane() == 0) {
+  a = wave_incl_scan64(a);
+  b = wave_incl_scan64(b);
+  if (lane() == 63) {
     red[wave()] = a;
     red[NW + wave()] = b;
   }
@@ -229,16 +207,16 @@ __device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_
   }
   bar();
 }
-// Exclusive prefix over the workgroup in thread order; `total` gets the sum of all.
+// Exclusive prefix over the workgroup in thread order; `total` gets the sum of all (red: NW).
 template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
-  uint32_t incl = wave_incl_scan(v);
+  const uint32_t incl = wave_incl_scan(v);
   if (lane() == 63) red[wave()] = incl;
   bar();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    uint32_t t = red[w];
+    const uint32_t t = red[w];
     base += (w < wave()) ? t : 0u;
     tot += t;
   }
@@ -246,29 +224,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
   total = tot;
   return base + incl - v;
 }
-
 // Argmax over the workgroup of (score, lowest id): every thread gets the winning id and
-// (through best_s) its score.
+// (through best_s) its score (reds, redi: NW entries each).
 template <int NW>
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
                                                 float* best_s = nullptr) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    float os = __shfl_xor(s, d, 64);
-    int32_t oi = __shfl_xor(id, d, 64);
-    bool take = (os > s) || (os == s && (uint32_t)oi < (uint32_t)id);
-    s = take ? os : s;
-    id = take ? oi : id;
-  }
-  if (lane() == 0) { reds[wave()] = s; redi[wave()] = id; }
+  wave_argmax(s, id);
+  if (lane() == 63) { reds[wave()] = s; redi[wave()] = id; }
   bar();
   float bs = reds[0];
   int32_t bi = redi[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    float os = reds[w];
-    int32_t oi = redi[w];
-    bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
+    const float os = reds[w];
+    const int32_t oi = redi[w];
+    const bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
     bs = take ? os : bs;
     bi = take ? oi : bi;
   }
@@ -286,10 +256,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-    const uint32_t hi_a = __umulhi(0xD2511F53u, c0), lo_a = 0xD2511F53u * c0;
-    const uint32_t hi_b = __umulhi(0xCD9E8D57u, c2), lo_b = 0xCD9E8D57u * c2;
-    const uint32_t n0 = hi_b ^ c1 ^ k0, n2 = hi_a ^ c3 ^ k1;
-    c0 = n0; c1 = lo_b; c2 = n2; c3 = lo_a;
+    const uint64_t pa = (uint64_t)0xD2511F53u * c0;   // one 32x32->64 multiply gives both halves
+    const uint64_t pb = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0, n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+    c0 = n0; c1 = (uint32_t)pb; c2 = n2; c3 = (uint32_t)pa;
   }
   return make_uint4(c0, c1, c2, c3);
 }
