@@ -38,16 +38,28 @@ def source_hash() -> str:
 
 
 def traffic_from_profiles():
-    """HBM bytes per launch from the committed PMC summary, if it matches the current kernel."""
-    path = os.path.join(ROOT, "profiles", "sample_rows_decode_traffic.json")
+    """HBM bytes per call from the committed PMC summary, if it was taken on the current kernels.
+
+    The summary (a text file) holds `key: value` lines; `source_hash` must equal the hash of
+    the kernel sources and `bytes_per_call` is FETCH_SIZE + WRITE_SIZE of the call's two
+    kernels, scaled by the copy-kernel calibration factor.
+    """
+    path = os.path.join(ROOT, "profiles", "sample_rows_decode_traffic.txt")
+    rec = {}
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                if ":" in line and not line.startswith(("#", " ")):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+    except OSError:
         return None
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return float(rec["bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(batch, budget_s: float = 12.0):
@@ -172,6 +184,19 @@ def main():
     torch.cuda.synchronize()
     warm_ms = np.array([a.elapsed_time(b) for a, b in warm])
 
+    # A plain device copy of one logits buffer: the known-size kernel that calibrates the
+    # FETCH_SIZE / WRITE_SIZE counters, and a read+write bandwidth reference.
+    cp = torch.empty_like(base)
+    cps = []
+    for i in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cp.copy_(bufs[i % ROTATE])
+        b.record(stream)
+        cps.append((a, b))
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([a.elapsed_time(b) for a, b in cps]))
+
     # A plain read of the same buffers (torch.sum) as a practical streaming ceiling.
     rd = []
     for i in range(min(args.steps, 100)):
@@ -213,6 +238,7 @@ def main():
         "graph_us_per_step": None if graph_ms_per_step is None else graph_ms_per_step * 1e3,
         "effective_GBps_median": BYTES_PER_CALL / (med * 1e-3) / 1e9,
         "torch_sum_read_GBps": BYTES_PER_CALL / (rd_ms * 1e-3) / 1e9,
+        "copy_read_write_GBps": 2 * BYTES_PER_CALL / (copy_ms * 1e-3) / 1e9,
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
