@@ -84,8 +84,10 @@ constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel t
 constexpr int kLdsCand = 8192;                      // candidates the row kernel holds in LDS
 constexpr int kVisU = 4;                            // LDS items per thread per visitor round
 constexpr int kGatherB = 12;                        // wave slices per gather batch
-constexpr int kMaxSeg = 2 * kRT;                    // wave slices per row the gather indexes
-static_assert(kDBins == 4 * kRT, "each row-kernel thread owns four histogram bins");
+constexpr int kMaxSeg = 1024;                       // wave slices per row the gather indexes
+constexpr int kSegPT = kMaxSeg / kRT;               // slice counts scanned per thread
+constexpr int kBPT = kDBins / kRT;                  // histogram bins owned per thread
+static_assert((kBPT == 2 || kBPT % 4 == 0) && kSegPT >= 1, "row-kernel geometry");
 
 // Summary of one wave's share of a chunk (32 bytes).
 struct WaveInfo {
@@ -199,18 +201,41 @@ __device__ __forceinline__ bool sel_member(const Sel& s, uint32_t rk, uint32_t i
 __device__ __forceinline__ Sel sel_all() { return Sel{0u, 32, 0xFFFFFFFFu}; }
 
 // ------------------------------------------------------------------ threshold-bin searches
-// Workgroup-wide searches over the kDBins-bin histograms; thread t owns bins 4t..4t+3 (one
-// conflict-free 16-byte LDS read), reads them and zeroes them for the next pass (no other
-// thread touches them before the next pass's atomics, which follow two barriers).
+// Workgroup-wide searches over the kDBins-bin histograms; thread t owns bins kBPT*t ..
+// kBPT*t + kBPT - 1 (16-byte LDS reads), reads them and zeroes them for the next pass (no
+// other thread touches them before the next pass's atomics, which follow two barriers).
 //
+// Reads thread t's kBPT count bins into c and zeroes them (16- or 8-byte LDS accesses).
+__device__ __forceinline__ void take_bins(uint32_t* hist, int t, uint32_t* c) {
+  if (kBPT == 2) {
+    uint2* h2 = reinterpret_cast<uint2*>(hist) + t;
+    const uint2 v = *h2;
+    c[0] = v.x;
+    c[1] = v.y;
+    *h2 = make_uint2(0, 0);
+  } else {
+    uint4* h4 = reinterpret_cast<uint4*>(hist) + t * (kBPT / 4);
+#pragma unroll
+    for (int q = 0; q < kBPT / 4; ++q) {
+      const uint4 v = h4[q];
+      c[4 * q] = v.x;
+      c[4 * q + 1] = v.y;
+      c[4 * q + 2] = v.z;
+      c[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int q = 0; q < kBPT / 4; ++q) h4[q] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // Count: the highest bin b with (count in bins >= b) >= need. Writes res[0] = b,
 // res[1] = count in bins > b, res[2] = count in b. Requires 1 <= need <= total.
 __device__ __forceinline__ void search_count(Smem& sm, uint32_t need) {
-  uint4* h4 = reinterpret_cast<uint4*>(sm.hist) + threadIdx.x;
-  const uint4 v = *h4;
-  *h4 = make_uint4(0, 0, 0, 0);
-  const uint32_t c[4] = {v.x, v.y, v.z, v.w};
-  const uint32_t lsum = v.x + v.y + v.z + v.w;
+  uint32_t c[kBPT];
+  take_bins(sm.hist, threadIdx.x, c);
+  uint32_t lsum = 0;
+#pragma unroll
+  for (int j = 0; j < kBPT; ++j) lsum += c[j];
   const uint32_t sfx = wave_incl_suffix(lsum);     // lanes >= this one, within the wave
   if (lane() == 0) sm.red[wave()] = sfx;
   bar();
@@ -220,48 +245,55 @@ __device__ __forceinline__ void search_count(Smem& sm, uint32_t need) {
   const uint32_t excl = above + sfx - lsum;        // count in bins above this thread's bins
   if (excl < need && excl + lsum >= need) {
     uint32_t acc = excl;
-    int j = 3;
+    int j = kBPT - 1;
     for (; j > 0; --j) {
       if (acc + c[j] >= need) break;
       acc += c[j];
     }
-    sm.res[0] = 4 * threadIdx.x + j;
+    sm.res[0] = kBPT * threadIdx.x + j;
     sm.res[1] = acc;
     sm.res[2] = c[j];
   }
   bar();
 }
 
-// Mass: the highest bin b with ma + (mass in bins >= b) >= target, masses exact (hi, lo)
-// sums compared after conversion to binary64. Writes res[0] = b, res[1] = count above,
-// res[2] = count in b, res64[0..1] = ma + mass above b, res64[2..3] = mass of b.
-__device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t ma_hi, uint64_t ma_lo, int S) {
+// Mass: the highest bin b with ma + (mass in bins >= b) >= target, masses exact fixed-point
+// sums compared after conversion to binary64. TWO: two 64-bit words per mass (hi, lo; the
+// row-streaming path, where K can be the whole row); otherwise one word (the candidate path,
+// |K| <= kFastK). Writes res[0] = b, res[1] = count above, res[2] = count in b,
+// res64[0..1] = ma + mass above b, res64[2..3] = mass of b (lo words 0 when !TWO).
+template <bool TWO>
+__device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t target_fx, uint64_t ma_hi,
+                                            uint64_t ma_lo, int S) {
   const int t = threadIdx.x;
-  uint4* h4 = reinterpret_cast<uint4*>(sm.hist) + t;
-  const uint4 cv = *h4;
-  *h4 = make_uint4(0, 0, 0, 0);
-  uint64_t mh[4], ml[4];
+  uint32_t c[kBPT];
+  uint64_t mh[kBPT], ml[kBPT];
+  take_bins(sm.hist, t, c);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    mh[j] = sm.mhi[4 * t + j];
-    ml[j] = sm.mlo[4 * t + j];
+  for (int j = 0; j < kBPT; ++j) {
+    mh[j] = sm.mhi[kBPT * t + j];
+    ml[j] = TWO ? sm.mlo[kBPT * t + j] : 0ull;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sm.mhi[4 * t + j] = 0;
-    sm.mlo[4 * t + j] = 0;
+  for (int j = 0; j < kBPT; ++j) {
+    sm.mhi[kBPT * t + j] = 0;
+    if (TWO) sm.mlo[kBPT * t + j] = 0;
   }
-  const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
-  const uint32_t lc = cv.x + cv.y + cv.z + cv.w;
-  const uint64_t lh = mh[0] + mh[1] + mh[2] + mh[3];
-  const uint64_t ll = ml[0] + ml[1] + ml[2] + ml[3];
+  uint32_t lc = 0;
+  uint64_t lh = 0, ll = 0;
+#pragma unroll
+  for (int j = 0; j < kBPT; ++j) {
+    lc += c[j];
+    lh += mh[j];
+    ll += ml[j];
+  }
   const uint32_t sc = wave_incl_suffix(lc);
   const uint64_t sh = wave_incl_suffix64(lh);
-  const uint64_t sl = wave_incl_suffix64(ll);
+  const uint64_t sl = TWO ? wave_incl_suffix64(ll) : 0ull;
   if (lane() == 0) {
     sm.red[wave()] = sc;
     sm.red64[wave()] = sh;
-    sm.red64[kRW + wave()] = sl;
+    if (TWO) sm.red64[kRW + wave()] = sl;
   }
   bar();
   uint32_t ac = 0;
@@ -271,22 +303,25 @@ __device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t ma
     const bool up = w > wave();
     ac += up ? sm.red[w] : 0u;
     ah += up ? sm.red64[w] : 0ull;
-    al += up ? sm.red64[kRW + w] : 0ull;
+    if (TWO) al += up ? sm.red64[kRW + w] : 0ull;
   }
+  // reaches(h, l): the mass (h, l) is >= the target -- in binary64 for two words, exactly in
+  // fixed point for one (target_fx = ceil(p * Z) in the same units)
+  auto reaches = [&](uint64_t h, uint64_t l) { return TWO ? mass_to_double(h, l, S) >= target : h >= target_fx; };
   uint32_t xc = ac + sc - lc;
   uint64_t xh = ma_hi + ah + sh - lh;
-  uint64_t xl = ma_lo + al + sl - ll;
-  const bool below = mass_to_double(xh, xl, S) < target;
-  const bool reach = mass_to_double(xh + lh, xl + ll, S) >= target;
+  uint64_t xl = TWO ? ma_lo + al + sl - ll : 0ull;
+  const bool below = !reaches(xh, xl);
+  const bool reach = reaches(xh + lh, xl + ll);
   if (below && reach) {
-    int j = 3;
+    int j = kBPT - 1;
     for (; j > 0; --j) {
-      if (mass_to_double(xh + mh[j], xl + ml[j], S) >= target) break;
+      if (reaches(xh + mh[j], xl + ml[j])) break;
       xh += mh[j];
       xl += ml[j];
       xc += c[j];
     }
-    sm.res[0] = 4 * t + j;
+    sm.res[0] = kBPT * t + j;
     sm.res[1] = xc;
     sm.res[2] = c[j];
     sm.res64[0] = xh;
@@ -397,8 +432,8 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
 // are zero on entry and on return. With `prebuilt`, the caller has already accumulated the
 // first pass (digit first_digit(hi_key, lo_key), counts and masses) and passed a barrier; it
 // may do so only when hi_key != lo_key.
-template <class KVis, class WMass>
-__device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, double target, int S,
+template <bool TWO, class KVis, class WMass>
+__device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, double target, uint64_t target_fx, int S,
                                            uint32_t n_in_play, uint32_t hi_key, uint32_t lo_key,
                                            uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept,
                                            bool prebuilt = false) {
@@ -421,13 +456,13 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
           const Mass q = wmass(rk);
           atomicAdd(&sm.hist[b], 1u);
           atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q.hi);
-          atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
+          if (TWO) atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
         }
       });
       bar();
     }
     counted = false;
-    search_mass(sm, target, ma_hi, ma_lo, S);
+    search_mass<TWO>(sm, target, target_fx, ma_hi, ma_lo, S);
     const uint32_t bin = sm.res[0];
     n_above += sm.res[1];
     tie_cnt = sm.res[2];
@@ -453,12 +488,20 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
       qh = q1.hi;
       ql = q1.lo;
     }
-    const double q = mass_to_double(qh, ql, S);
-    const double ma = mass_to_double(ma_hi, ma_lo, S);
-    const double j = q > 0.0 ? ceil((target - ma) / q) : (double)tie_cnt;
-    uint32_t t = (uint32_t)fmin(fmax(j, 1.0), (double)tie_cnt);
-    while (t > 1 && mass_to_double(ma_hi + qh * (t - 1), ma_lo + ql * (t - 1), S) >= target) --t;
-    while (t < tie_cnt && mass_to_double(ma_hi + qh * t, ma_lo + ql * t, S) < target) ++t;
+    auto reaches = [&](uint64_t h, uint64_t l) { return TWO ? mass_to_double(h, l, S) >= target : h >= target_fx; };
+    uint32_t t;
+    if (TWO) {
+      const double q = mass_to_double(qh, ql, S);
+      const double ma = mass_to_double(ma_hi, ma_lo, S);
+      const double j = q > 0.0 ? ceil((target - ma) / q) : (double)tie_cnt;
+      t = (uint32_t)fmin(fmax(j, 1.0), (double)tie_cnt);
+    } else {   // exact: the fewest t with ma + t * q >= target_fx
+      const uint64_t rest = target_fx > ma_hi ? target_fx - ma_hi : 0ull;
+      const uint64_t j = qh > 0 ? (rest + qh - 1) / qh : (uint64_t)tie_cnt;
+      t = (uint32_t)min(max(j, (uint64_t)1), (uint64_t)tie_cnt);
+    }
+    while (t > 1 && reaches(ma_hi + qh * (t - 1), ma_lo + ql * (t - 1))) --t;
+    while (t < tie_cnt && !reaches(ma_hi + qh * t, ma_lo + ql * t)) ++t;
     take = t;
   }
   Sel s{prefix, lo, 0xFFFFFFFFu};
@@ -979,26 +1022,34 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
   uint32_t kept = nk;
   if (rp.p != 1.0f) {
     // One visit of K computes every weight once: Z, and the counts and masses of the mass
-    // select's first pass.
+    // select's first pass. |K| <= kFastK, so one 64-bit word floor(w * 2^S) per weight sums
+    // exactly (S = 63 - bitlen(|K|) >= 51; truncation costs < |K| * 2^-S of Z).
     const int S = 63 - bitlen(nk);
-    auto wmass = [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); };
+    auto wmass = [&](uint32_t rk) { return Mass{mass1_of(weight_of(rk, m, t), S), 0ull}; };
     const Digit g = first_digit(kmax, klo);
     const bool pre = g.lo > 0;
     uint64_t zh = 0, zl = 0;
     kvis([&](uint32_t rk, uint32_t) {
-      const Mass q = wmass(rk);
-      zh += q.hi;
-      zl += q.lo;
+      const uint64_t q = mass1_of(weight_of(rk, m, t), S);
+      zh += q;
       if (pre) {
         const uint32_t b = (rk >> g.sh) & g.dm;
         atomicAdd(&sm.hist[b], 1u);
-        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q.hi);
-        atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
+        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q);
       }
     });
     block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics
-    const double target = (double)rp.p * mass_to_double(zh, zl, S);
-    sp = select_mass(kvis, wmass, target, S, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
+    // [TOPP] reference steps 4-5 in exact fixed point: keep the shortest prefix whose mass is
+    // >= p * Z, i.e. >= ceil(p * Z) since masses are integers; p = mant * 2^-sh (mant < 2^24).
+    int pe;
+    const float pf = frexpf(rp.p, &pe);                       // rp.p = pf * 2^pe, pf in [0.5, 1)
+    const uint64_t mant = (uint64_t)ldexpf(pf, 24);
+    const int psh = 24 - pe;                                  // > 24 since p < 1
+    const unsigned __int128 prod = (unsigned __int128)mant * zh;
+    const uint64_t target_fx = psh >= 128 ? (prod != 0 ? 1ull : 0ull)
+                                          : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
+    const double target = (double)rp.p * ldexp((double)zh, -S);   // unused by the one-word search
+    sp = select_mass<false>(kvis, wmass, target, target_fx, S, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -1114,7 +1165,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
     block_sum2_u64<kRW>(zh, zl, sm.red64);
     const double target = (double)rp.p * mass_to_double(zh, zl, S);
     const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
-    sp = select_mass(kvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, S, ke,
+    sp = select_mass<true>(kvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, 0ull, S, ke,
                      kmax, klo, 0u, V - 1, sm, kept);
   }
   if (MODE == kModeTopp) {
@@ -1160,7 +1211,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   const RowPlan rp = plan_row(P, MODE, r);
   const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
   // zero the histograms (each select leaves them zero again)
-  reinterpret_cast<uint4*>(sm.hist)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < kDBins / 4; i += kRT) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kDBins / 2; i += kRT) {
     reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
     reinterpret_cast<uint4*>(sm.mlo)[i] = make_uint4(0, 0, 0, 0);
@@ -1230,15 +1281,22 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
 
   if (path == kPathCand && nseg <= kMaxSeg && !P.force_exact && (flags & kFlagOverflow) == 0) {
     const uint32_t ke = (uint32_t)rp.k_eff;
-    // exclusive prefix of the slice counts (two consecutive slices per thread): the
+    // exclusive prefix of the slice counts (kSegPT consecutive slices per thread): the
     // candidates' flat, id-ordered index space
-    const int s0 = 2 * (int)threadIdx.x;
-    const uint32_t c0 = s0 < nseg ? sm.segoff[s0] : 0u;
-    const uint32_t c1 = s0 + 1 < nseg ? sm.segoff[s0 + 1] : 0u;
+    const int s0 = kSegPT * (int)threadIdx.x;
+    uint32_t cs[kSegPT], csum = 0;
+#pragma unroll
+    for (int q = 0; q < kSegPT; ++q) {
+      cs[q] = s0 + q < nseg ? sm.segoff[s0 + q] : 0u;
+      csum += cs[q];
+    }
     uint32_t total;
-    const uint32_t off = block_excl_scan<kRW>(c0 + c1, sm.red, total);   // barrier before writes
-    if (s0 < nseg) sm.segoff[s0] = off;
-    if (s0 + 1 < nseg) sm.segoff[s0 + 1] = off + c0;
+    uint32_t off = block_excl_scan<kRW>(csum, sm.red, total);   // barrier before the writes
+#pragma unroll
+    for (int q = 0; q < kSegPT; ++q) {
+      if (s0 + q < nseg) sm.segoff[s0 + q] = off;
+      off += cs[q];
+    }
     if (threadIdx.x == 0) sm.segoff[nseg] = total;
     if (total >= ke && total <= (uint32_t)kLdsCand) {
       bar();

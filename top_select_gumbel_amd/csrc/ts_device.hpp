@@ -127,24 +127,14 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   v |= dpp32<0x143, 0xc>(v, 0u);
   return wave_total(v);
 }
-// One step of the argmax combine of (score, lowest id); a lane without a source sees
-// (-inf, INT_MAX), which never wins.
-template <int CTRL, int RMASK>
-__device__ __forceinline__ void argmax_step(float& s, int32_t& id) {
-  const float os = __uint_as_float(dpp32<CTRL, RMASK>(__float_as_uint(s), __float_as_uint(-INFINITY)));
-  const int32_t oi = (int32_t)dpp32<CTRL, RMASK>((uint32_t)id, 0x7FFFFFFFu);
-  const bool take = (os > s) || (os == s && (uint32_t)oi < (uint32_t)id);
-  s = take ? os : s;
-  id = take ? oi : id;
-}
-// Argmax of (score, lowest id) over the wave; the result is in lane 63.
+// Argmax of (score, lowest id) over the wave, every lane gets it: the maximum of the ordered
+// score keys, then the minimum id among the lanes holding it -- two plain unsigned DPP
+// reductions (a combined compare-and-select per step costs three times as much).
 __device__ __forceinline__ void wave_argmax(float& s, int32_t& id) {
-  argmax_step<0x111, 0xf>(s, id);
-  argmax_step<0x112, 0xf>(s, id);
-  argmax_step<0x114, 0xf>(s, id);
-  argmax_step<0x118, 0xf>(s, id);
-  argmax_step<0x142, 0xa>(s, id);
-  argmax_step<0x143, 0xc>(s, id);
+  const uint32_t k = f2key(s);
+  const uint32_t km = wave_max(k);
+  id = (int32_t)wave_min(k == km ? (uint32_t)id : 0xFFFFFFFFu);
+  s = key2f(km);
 }
 
 // ---------------------------------------------------------------- block reductions
@@ -225,26 +215,23 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
   return base + incl - v;
 }
 // Argmax over the workgroup of (score, lowest id): every thread gets the winning id and
-// (through best_s) its score (reds, redi: NW entries each).
+// (through best_s) its score (reds, redi: NW entries each). A score of -inf loses to every
+// finite one; scores are never NaN.
 template <int NW>
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
                                                 float* best_s = nullptr) {
   wave_argmax(s, id);
-  if (lane() == 63) { reds[wave()] = s; redi[wave()] = id; }
+  if (lane() == 0) { reds[wave()] = s; redi[wave()] = id; }
   bar();
-  float bs = reds[0];
-  int32_t bi = redi[0];
+  uint32_t km = 0;
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    const float os = reds[w];
-    const int32_t oi = redi[w];
-    const bool take = (os > bs) || (os == bs && (uint32_t)oi < (uint32_t)bi);
-    bs = take ? os : bs;
-    bi = take ? oi : bi;
-  }
+  for (int w = 0; w < NW; ++w) km = max(km, f2key(reds[w]));
+  uint32_t bi = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) bi = (f2key(reds[w]) == km) ? min(bi, (uint32_t)redi[w]) : bi;
   bar();
-  if (best_s) *best_s = bs;
-  return bi;
+  if (best_s) *best_s = key2f(km);
+  return (int32_t)bi;
 }
 
 // ---------------------------------------------------------------- Philox4x32-10
@@ -293,5 +280,7 @@ __device__ __forceinline__ Mass mass_of(double w, int s) {
 __device__ __forceinline__ double mass_to_double(uint64_t hi, uint64_t lo, int s) {
   return ldexp((double)hi, -s) + ldexp((double)lo, -2 * s);
 }
+// One-word form for sets of at most 2^(63-S) weights: floor(w * 2^S), exact to truncation.
+__device__ __forceinline__ uint64_t mass1_of(double w, int s) { return (uint64_t)ldexp(w, s); }
 
 }  // namespace tsd
