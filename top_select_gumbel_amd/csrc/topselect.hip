@@ -589,6 +589,24 @@ __device__ __forceinline__ void lds_for(const uint32_t* ka, const uint32_t* ia, 
   }
 }
 
+// lds_for over K = (kkey, kidx)[0, n) that also passes each item's position: f(i, key, id).
+template <class F>
+__device__ __forceinline__ void kvis_i(uint32_t n, F f, Smem& sm) {
+  for (uint32_t base = threadIdx.x; base < n; base += kRT * kVisU) {
+    uint32_t k[kVisU], x[kVisU];
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      const uint32_t i = min(base + u * kRT, n - 1);   // clamped: in bounds, result unused past n
+      k[u] = sm.kkey[i];
+      x[u] = sm.kidx[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      if (base + u * kRT < n) f(base + u * kRT, k[u], x[u]);
+    }
+  }
+}
+
 // Append the items of [0, n) of (ka, ia) that satisfy `mem` to (dkey, didx), in any order:
 // per round, a wave scan of the per-lane counts and one LDS atomic per wave reserve room.
 // Returns the count (entries past `cap` are dropped). Ends with a barrier. Successive calls
@@ -792,7 +810,8 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   // (a quarter of the chunk spread over four segments), so it is known while the rest of
   // the chunk is still arriving. Any threshold is correct (the row kernel certifies); the
   // margin only makes a failed certification rare: the sample's count above the row's k-th
-  // key has mean mu = k * ns / V, and the threshold sits mu + 6 sqrt(mu) + 10 keys down.
+  // key has mean mu = k * ns / V, and the threshold sits mu + 5 sqrt(mu) + 5 keys down (a
+  // Poisson tail below 1e-7 per workgroup for every k up to the fast path's limit).
   // Work happens on the fp32 values: a key >= threshold-key test is a float >= test against
   // the threshold's float (ordered keys are a monotone map of fp32, with -0 == +0 in both).
   // The threshold is located in two levels: a 2048-bin histogram of the top 11 key bits, then
@@ -819,7 +838,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
       ns += (uint32_t)max(e_hi - 4 * lo_q, 0);
     }
     const float mu = (float)rp.k_eff * (float)ns / (float)P.V;
-    const uint32_t jt = (uint32_t)ceilf(mu + 6.0f * sqrtf(mu) + 10.0f);
+    const uint32_t jt = (uint32_t)ceilf(mu + 5.0f * sqrtf(mu) + 5.0f);
     if (jt < ns) {
       bar();   // sample histogram complete
       if (w == 0) search_hist(sm.hist, jt, sm);
@@ -1018,6 +1037,8 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
   const float m = key2f(kmax);
   const float t = rp.t;
   auto kvis = [&](auto f) { lds_for(sm.kkey, sm.kidx, nk, f); };
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  float* const gsc = reinterpret_cast<float*>(sm.ckey);   // Gumbel scores, gsc[i] for item i of K
   Sel sp = sel_all();
   uint32_t kept = nk;
   if (rp.p != 1.0f) {
@@ -1028,17 +1049,34 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
     auto wmass = [&](uint32_t rk) { return Mass{mass1_of(weight_of(rk, m, t), S), 0ull}; };
     const Digit g = first_digit(kmax, klo);
     const bool pre = g.lo > 0;
+    // When sampling, the same visit draws every item's Gumbel score into gsc[i] (the
+    // candidate keys are dead once K is compacted), so the draw overlaps the mass select
+    // and no kept-set compaction is needed.
     uint64_t zh = 0, zl = 0;
-    kvis([&](uint32_t rk, uint32_t) {
-      const uint64_t q = mass1_of(weight_of(rk, m, t), S);
-      zh += q;
-      if (pre) {
-        const uint32_t b = (rk >> g.sh) & g.dm;
-        atomicAdd(&sm.hist[b], 1u);
-        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q);
+    for (uint32_t base = threadIdx.x; base < nk; base += kRT * kVisU) {
+      uint32_t kr[kVisU], kx[kVisU];
+#pragma unroll
+      for (int u = 0; u < kVisU; ++u) {
+        const uint32_t i = min(base + u * kRT, nk - 1);   // clamped: in bounds, unused past nk
+        kr[u] = sm.kkey[i];
+        kx[u] = sm.kidx[i];
       }
-    });
-    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics
+#pragma unroll
+      for (int u = 0; u < kVisU; ++u) {
+        const uint32_t i = base + u * kRT;
+        if (i < nk) {
+          const uint64_t q = mass1_of(weight_of(kr[u], m, t), S);
+          zh += q;
+          if (pre) {
+            const uint32_t b = (kr[u] >> g.sh) & g.dm;
+            atomicAdd(&sm.hist[b], 1u);
+            atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q);
+          }
+          if (MODE == kModeSample) gsc[i] = gumbel_score(kr[u], kx[u], m, t, (uint32_t)r, k0, k1);
+        }
+      }
+    }
+    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics and stores
     // [TOPP] reference steps 4-5 in exact fixed point: keep the shortest prefix whose mass is
     // >= p * Z, i.e. >= ceil(p * Z) since masses are integers; p = mant * 2^-sh (mant < 2^24).
     int pe;
@@ -1060,25 +1098,23 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
       });
     }
   } else {
-    // Gumbel scores only for the kept set: compact it (into the candidate arrays, no longer
-    // needed) so that only ceil(|P| / 64) waves draw noise.
-    uint32_t nkept = nk;
-    const uint32_t* gk = sm.kkey;
-    const uint32_t* gi = sm.kidx;
-    if (rp.p != 1.0f) {
-      nkept = min(append_members(sm.kkey, sm.kidx, nk, [&](uint32_t rk, uint32_t idx) { return sel_member(sp, rk, idx); },
-                                 sm.ckey, sm.cidx, (uint32_t)kLdsCand, 1, sm),
-                  (uint32_t)kLdsCand);
-      gk = sm.ckey;
-      gi = sm.cidx;
-    }
-    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    // Gumbel-max over the kept set P: the scores drawn above, masked by membership of P;
+    // without top-p P = K and the scores are drawn here.
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
-    for (uint32_t i = threadIdx.x; i < nkept; i += kRT) {
-      const uint32_t idx = gi[i];
-      const float sc = gumbel_score(gk[i], idx, m, t, (uint32_t)r, k0, k1);
-      if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
+    if (rp.p != 1.0f) {
+      kvis_i(nk, [&](uint32_t i, uint32_t rk, uint32_t idx) {
+        if (sel_member(sp, rk, idx)) {
+          const float sc = gsc[i];
+          if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
+        }
+      }, sm);
+    } else {
+      for (uint32_t i = threadIdx.x; i < nk; i += kRT) {
+        const uint32_t idx = sm.kidx[i];
+        const float sc = gumbel_score(sm.kkey[i], idx, m, t, (uint32_t)r, k0, k1);
+        if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
+      }
     }
     const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
     if (threadIdx.x == 0) P.out_token[r] = tok;
