@@ -83,7 +83,8 @@ constexpr int kDBits = 11;                          // radix digit of the row se
 constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel thread
 constexpr int kLdsCand = 8192;                      // candidates the row kernel holds in LDS
 constexpr int kVisU = 4;                            // LDS items per thread per visitor round
-constexpr int kGatherB = 12;                        // wave slices per gather batch
+constexpr int kGatherB = 12;
+constexpr uint32_t kSmallBin = 64;                  // boundary bins up to this size are resolved by one wave                        // wave slices per gather batch
 constexpr int kMaxSeg = 1024;                       // wave slices per row the gather indexes
 constexpr int kSegPT = kMaxSeg / kRT;               // slice counts scanned per thread
 constexpr int kBPT = kDBins / kRT;                  // histogram bins owned per thread
@@ -153,6 +154,11 @@ struct Smem {
   uint32_t res[4];
   uint64_t res64[4];
   uint32_t kcount[2];
+  uint32_t bkey[kSmallBin];    // a small boundary bin, collected for one wave to rank
+  uint32_t bidx[kSmallBin];
+  uint64_t bmass[kSmallBin];
+  uint32_t bres[4];
+  uint32_t bcount;             // zero outside collect_bin .. its resolution
 };
 
 // LDS of the stream kernel (about 20 KB)
@@ -351,6 +357,63 @@ __device__ __forceinline__ Digit first_digit(uint32_t hi_rk, uint32_t lo_rk) {
   return g;
 }
 
+// ------------------------------------------------------------------ small boundary bins
+// When a radix pass leaves c <= kSmallBin items in the boundary bin, one visit collects
+// them and wave 0 ranks them directly (key descending, then id ascending: the row order),
+// in place of further passes over the whole set.
+template <class Vis>
+__device__ __forceinline__ void collect_bin(const Vis& vis, uint32_t prefix, int lo, Smem& sm) {
+  vis([&](uint32_t rk, uint32_t idx) {
+    if (shr(rk, lo) == prefix) {
+      const uint32_t p = atomicAdd(&sm.bcount, 1u);
+      if (p < kSmallBin) {
+        sm.bkey[p] = rk;
+        sm.bidx[p] = idx;
+      }
+    }
+  });
+  bar();
+}
+
+// Wave 0: lane l < c loads collected item l into (k, x) and returns its rank, the number of
+// collected items before it in the row order (a permutation of 0 .. c-1 since ids differ).
+__device__ __forceinline__ uint32_t bin_rank(uint32_t c, uint32_t& k, uint32_t& x, const Smem& sm) {
+  const uint32_t l = (uint32_t)lane();
+  k = 0u;
+  x = 0xFFFFFFFFu;
+  if (l < c) {
+    k = sm.bkey[l];
+    x = sm.bidx[l];
+  }
+  uint32_t rank = 0;
+  const uint32_t cu = (uint32_t)__builtin_amdgcn_readfirstlane((int)c);   // uniform trip count
+  for (uint32_t j = 0; j < cu; ++j) {
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)k, (int)j);
+    const uint32_t xj = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
+    rank += (kj > k || (kj == k && xj < x)) ? 1u : 0u;
+  }
+  return rank;
+}
+
+// The `need` first (row order) of the c collected items of the bin (prefix, lo): the
+// selection is every key above the need-th item, and that item's equal keys up to its id.
+template <class Vis>
+__device__ __forceinline__ Sel small_topk(const Vis& vis, uint32_t prefix, int lo, uint32_t c, uint32_t need,
+                                          Smem& sm) {
+  collect_bin(vis, prefix, lo, sm);
+  if (wave() == 0) {
+    uint32_t k, x;
+    const uint32_t rank = bin_rank(c, k, x, sm);
+    if ((uint32_t)lane() < c && rank == need - 1u) {
+      sm.bres[0] = k;
+      sm.bres[1] = x;
+    }
+    if (lane() == 0) sm.bcount = 0;
+  }
+  bar();
+  return Sel{sm.bres[0], 0, sm.bres[1]};
+}
+
 // ------------------------------------------------------------------ exact count select
 // MSB-first radix select of the `need` largest radix keys among the items the visitor
 // yields (vis(f) calls f(rk, idx) for this thread's items; the union over threads must be
@@ -404,7 +467,38 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
                                            bool prebuilt = false) {
   Sel s;
   uint32_t eq_take, tie_cnt;
-  count_select(vis, need, n_in_play, hi_key, lo_key, sm, s.prefix, s.lo, eq_take, tie_cnt, prebuilt);
+  {
+    // count_select's passes, leaving early for a small boundary bin
+    int lo = (hi_key == lo_key) ? 0 : 32 - __clz((int)(hi_key ^ lo_key));
+    uint32_t prefix = shr(hi_key, lo);
+    tie_cnt = n_in_play;
+    bool counted = prebuilt;
+    while (lo > 0 && need > 0) {
+      const int d = min(kDBits, lo);
+      const int sh = lo - d;
+      const uint32_t dm = (1u << d) - 1u;
+      const uint32_t pre = prefix;
+      const int lo_now = lo;
+      if (!counted) {
+        vis([&](uint32_t rk, uint32_t) {
+          if (shr(rk, lo_now) == pre) atomicAdd(&sm.hist[(rk >> sh) & dm], 1u);
+        });
+        bar();
+      }
+      counted = false;
+      search_count(sm, need);
+      const uint32_t bin = sm.res[0], above = sm.res[1], cnt = sm.res[2];
+      need -= above;
+      prefix = (prefix << d) | bin;
+      lo = sh;
+      tie_cnt = cnt;
+      if (cnt == need) break;
+      if (cnt <= kSmallBin) return small_topk(vis, prefix, lo, cnt, need, sm);
+    }
+    s.prefix = prefix;
+    s.lo = lo;
+    eq_take = need;
+  }
   s.cutoff = 0xFFFFFFFFu;
   if (eq_take < tie_cnt) {
     // the eq_take lowest ids among the tied items: select on ~id
@@ -473,6 +567,33 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
     prefix = (prefix << d) | bin;
     lo = sh;
     if (tie_cnt == 1) { single = true; break; }
+    if (!TWO && tie_cnt <= kSmallBin) {
+      // Rank the bin's items, lay their masses out in row order, and cut at the first
+      // prefix whose mass (above the bin plus the prefix) reaches the target.
+      collect_bin(kvis, prefix, lo, sm);
+      if (wave() == 0) {
+        uint32_t k, x;
+        const uint32_t c = tie_cnt;
+        const uint32_t rank = bin_rank(c, k, x, sm);
+        const bool in = (uint32_t)lane() < c;
+        if (in) sm.bmass[rank] = wmass(k).hi;
+        wave_lds_sync();
+        const uint64_t cum = wave_incl_scan64(in ? sm.bmass[lane()] : 0ull);
+        const uint64_t hit = __ballot(in && ma_hi + cum >= target_fx);
+        const uint32_t j = hit ? (uint32_t)__builtin_ctzll(hit) : c - 1u;   // the bin reaches it
+        if (in && rank == j) {
+          sm.bres[0] = k;
+          sm.bres[1] = x;
+        }
+        if (lane() == 0) {
+          sm.bres[2] = j + 1u;
+          sm.bcount = 0;
+        }
+      }
+      bar();
+      kept = n_above + sm.bres[2];
+      return Sel{sm.bres[0], 0, sm.bres[1]};
+    }
   }
   uint32_t take = 1;
   if (!single && tie_cnt > 1) {
@@ -1246,7 +1367,8 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   }
   const RowPlan rp = plan_row(P, MODE, r);
   const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
-  // zero the histograms (each select leaves them zero again)
+  // zero the histograms (each select leaves them zero again) and the small-bin counter
+  if (threadIdx.x == 0) sm.bcount = 0;
   for (int i = threadIdx.x; i < kDBins / 4; i += kRT) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kDBins / 2; i += kRT) {
     reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
