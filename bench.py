@@ -80,6 +80,96 @@ def cpu_baseline(batch, budget_s: float = 12.0):
                       f"single process, {os.cpu_count()} host cpus visible"}
 
 
+# The other workloads: (generator, op, input buffers rotated so that each call reads cold
+# data from HBM: R * bytes >= 512 MB where it fits, the MALL being 256 MB).
+OTHER_CONFIGS = {
+    "tiny": ("tiny", "sample", 4),
+    "heavy": ("heavy", "sample", 16),
+    "tie_stress": ("tie_stress", "sample", 8),
+    "indexer_rows": ("indexer_rows", "topk", 32),
+    "indexer_long": ("indexer_long", "topk", 128),
+    "indexer_near_uniform": ("indexer_near_uniform", "topk", 900),
+}
+
+
+def other_config(name, args):
+    """Time one non-headline workload: one JSON line of per-call kernel time and rates."""
+    import numpy as np
+    import torch
+
+    import top_select_gumbel_amd as ts
+    from top_select_gumbel_amd import workloads as wl
+
+    gen, op, rot = OTHER_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    lib = ts.load_library()
+    b = getattr(wl, gen)()
+    rows, vocab = b.logits.shape
+    base = torch.from_numpy(b.logits).to(dev)
+    bufs = [base] + [torch.roll(base, shifts=37 * i, dims=1).contiguous() for i in range(1, rot)]
+    st = torch.empty(rows, dtype=torch.int32, device=dev)
+    k = torch.from_numpy(b.k).to(dev)
+    if op == "sample":
+        p = torch.from_numpy(b.p).to(dev)
+        t = torch.from_numpy(b.t).to(dev)
+        seeds = b.seeds if b.seeds is not None else wl.heavy_launch_seeds(0, rows)
+        s = torch.from_numpy(seeds.view(np.int64)).to(dev)
+        tok = torch.empty(rows, dtype=torch.int32, device=dev)
+        nb = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, rows, vocab, 0)
+        ws = ts.workspace(nb, dev)
+        fixed = (k.data_ptr(), p.data_ptr(), t.data_ptr(), s.data_ptr(), tok.data_ptr(), st.data_ptr(),
+                 ws.data_ptr(), ws.numel())
+        call = lambda x, h: lib.ts_sample_rows(x, rows, vocab, vocab, *fixed, h)
+        cname = "ts_sample_rows"
+    else:
+        out = torch.empty((rows, b.k_max), dtype=torch.int32, device=dev)
+        nb = lib.ts_workspace_bytes(ts.TS_OP_TOPK_SELECT, rows, vocab, b.k_max)
+        ws = ts.workspace(nb, dev)
+        call = lambda x, h: lib.ts_topk_select(x, rows, vocab, vocab, k.data_ptr(), b.k_max, out.data_ptr(),
+                                               st.data_ptr(), ws.data_ptr(), ws.numel(), h)
+        cname = "ts_topk_select"
+    ptrs = [x.data_ptr() for x in bufs]
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def timed(n, warm):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            rc = call(ptrs[0] if warm else ptrs[i % rot], h)
+            ev[i][1].record(stream)
+            if rc:
+                raise RuntimeError(ts.ts_last_error())
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(e) for a, e in ev]) * 1e3   # us
+
+    for i in range(args.warmup):
+        call(ptrs[i % rot], h)
+    torch.cuda.synchronize()
+    us = timed(args.steps, False)
+    warm_us = timed(min(args.steps, 200), True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(ptrs[i % rot], h)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / args.steps * 1e6
+    assert int(st.abs().sum()) == 0, "rows reported errors"
+    nbytes = rows * vocab * 4
+    med = float(np.median(us))
+    print(json.dumps({
+        "config": name, "op": cname, "rows": rows, "vocab": vocab, "input_buffers": rot,
+        "bytes_per_call": nbytes, "steps": args.steps, "warmup": args.warmup,
+        "kernel_us": {"median": med, "p10": float(np.percentile(us, 10)), "p90": float(np.percentile(us, 90))},
+        "warm_kernel_us_median": float(np.median(warm_us)),
+        "back_to_back_us_per_call": wall_us,
+        "rows_per_s": rows / (wall_us * 1e-6),
+        "effective_GBps_median": nbytes / (med * 1e-6) / 1e9,
+        "frac_of_8TBps": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "source_hash": source_hash(),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,12 +177,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-only", action="store_true")
+    ap.add_argument("--config", default="decode", choices=["decode"] + sorted(OTHER_CONFIGS),
+                    help="decode (the headline line) or one of the other workloads, timed alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "rows are independent, so N GPUs would each take B/N rows of the same kernel.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.config != "decode":
+        other_config(args.config, args)
+        return
 
     import numpy as np
     import torch

@@ -155,6 +155,27 @@ def test_topk_indexer_long_and_near_uniform():
         check_topk(b.logits, b.k, 2048, out, st, b.name)
 
 
+def test_topk_long_rows_global_candidates():
+    # More candidates than LDS holds (1M-element rows, k=2048): row 0 takes the filtered
+    # gather from the slices in global memory; row 1 has 40000 ties at its maximum, so every
+    # candidate key is equal and the first k by id are taken; row 2 puts 20000 items on each
+    # of two adjacent fp32 values, the filtered set is still too large and the row takes the
+    # exact path from the smallest workgroup threshold.
+    rng = np.random.default_rng(91)
+    n = 1 << 20
+    x = np.round(rng.standard_normal((3, n)), 3).astype(np.float32)
+    x[1, rng.choice(n, 40000, replace=False)] = np.float32(9.0)
+    v0 = np.float32(7.0)
+    v1 = np.nextafter(v0, np.float32(8.0))
+    pos = rng.choice(n, 40000, replace=False)
+    x[2, pos[:20000]] = v0
+    x[2, pos[20000:]] = v1
+    k = np.array([2048, 2048, 2048], np.int32)
+    banner("topk 3x1048576 k=2048: filtered gather, all-equal cut, exact fallback")
+    out, st = run_topk(x, k, 2048)
+    check_topk(x, k, 2048, out, st, "long")
+
+
 def test_topk_deterministic_and_path_invariant():
     banner("topk repeat + chunk-size forcing")
     b = wl.small_random(9, 6, 90000, 2048, tie_levels=50)
@@ -281,6 +302,23 @@ def test_sample_heavy_rows_match_oracle():
     banner("sample heavy-tailed 8x32000 (full-row path)")
     tok, st = run_sample(b.logits, b.k, b.p, b.t, seeds)
     check_samples(b.logits, b.k, b.p, b.t, seeds, tok, st, None, "heavy")
+
+
+def test_topp_and_sample_long_rows_global_candidates():
+    # 1M-element rows whose candidates exceed LDS: top-p and sampling after the filtered
+    # gather from global memory.
+    rng = np.random.default_rng(92)
+    n = 1 << 20
+    x = (rng.standard_normal((2, n)) * 2.5).astype(np.float32)
+    k = np.array([2048, 1500], np.int32)
+    p = np.array([0.9, 0.97], np.float32)
+    t = np.array([1.0, 0.7], np.float32)
+    seeds = rng.integers(0, 2 ** 64, 2, dtype=np.uint64)
+    banner("topp + sample 2x1048576 k=2048/1500 (filtered gather)")
+    kept, mask, st = run_topp(x, k, p, t, want_mask=True)
+    check_topp(x, k, p, t, kept, mask, st, "long")
+    tok, st = run_sample(x, k, p, t, seeds)
+    check_samples(x, k, p, t, seeds, tok, st, kept, "long")
 
 
 def test_sample_deterministic_and_path_invariant():

@@ -74,7 +74,8 @@ constexpr int kH2Bits = 8;                          // second-level digit inside
 constexpr int kH2Bins = 1 << kH2Bits;
 constexpr int kSampleSlots = 2;                     // slots whose keys form the sample
 constexpr int kQStage = 128;                        // staged quads per wave
-constexpr int kCapW = 512;                          // candidate slots per wave in the workspace
+constexpr int kCapW = kChunkMax / kW1;              // candidate slots per wave: its whole share, so a
+                                                     // slice cannot overflow (massive ties stay exact)
 // row kernel
 constexpr int kRT = 512;                            // threads per row workgroup
 constexpr int kRW = kRT / 64;
@@ -357,6 +358,20 @@ __device__ __forceinline__ Digit first_digit(uint32_t hi_rk, uint32_t lo_rk) {
   return g;
 }
 
+// ------------------------------------------------------------------ histogram adds
+// Count-histogram increment by the calling (active) lanes. When every active lane hits the
+// same bin (runs of equal keys), one lane adds their number: same-address LDS atomics from
+// a whole wave would otherwise serialize.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t b) {
+  const uint64_t act = __ballot(1);
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+  if (__ballot(b == b0) == act) {
+    if ((uint32_t)lane() == (uint32_t)__builtin_ctzll(act)) atomicAdd(&h[b0], (uint32_t)__popcll(act));
+  } else {
+    atomicAdd(&h[b], 1u);
+  }
+}
+
 // ------------------------------------------------------------------ small boundary bins
 // When a radix pass leaves c <= kSmallBin items in the boundary bin, one visit collects
 // them and wave 0 ranks them directly (key descending, then id ascending: the row order),
@@ -443,7 +458,7 @@ __device__ __forceinline__ void count_select(const Vis& vis, uint32_t need, uint
     uint32_t* hist = sm.hist;
     if (!counted) {
       vis([&](uint32_t rk, uint32_t) {
-        if (shr(rk, lo_now) == pre) atomicAdd(&hist[(rk >> sh) & dm], 1u);
+        if (shr(rk, lo_now) == pre) hist_add(hist, (rk >> sh) & dm);
       });
       bar();
     }
@@ -481,7 +496,7 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
       const int lo_now = lo;
       if (!counted) {
         vis([&](uint32_t rk, uint32_t) {
-          if (shr(rk, lo_now) == pre) atomicAdd(&sm.hist[(rk >> sh) & dm], 1u);
+          if (shr(rk, lo_now) == pre) hist_add(sm.hist, (rk >> sh) & dm);
         });
         bar();
       }
@@ -1348,6 +1363,140 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   }
 }
 
+// The row's candidates when there are more than LDS holds: they stay in their slices in
+// global memory (sm.segoff holds the slices' exclusive offsets and the total). One pass
+// counts their first digit over [cmin, kmax] and finds the bin holding the ke-th largest;
+// the candidates with keys at or above that bin's low edge (a superset of the candidates'
+// top ke) are then counted per slice and gathered into LDS in id order. When every
+// candidate key is equal, the first ke in id order are gathered directly. Returns the
+// number gathered, 0 when they would not fit; *lo_key is a lower bound of their keys.
+__device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int nseg, uint32_t ke, uint32_t kmax,
+                                                    uint32_t cmin, Smem& sm, uint32_t* lo_key) {
+  const uint2* base = P.cand + (int64_t)r * nseg * P.cap_w;
+  const uint32_t j = (uint32_t)lane();
+  // per_batch(sb, cnt, first, gs): kGatherB slices sb, sb + kRW, ... of this wave, with
+  // entry `lane` of each already loaded into first[u]
+  auto batches = [&](auto per_batch) {
+    for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
+      uint32_t cnt[kGatherB];
+#pragma unroll
+      for (int u = 0; u < kGatherB; ++u) {
+        const int sl = min(sb + u * kRW, nseg);   // slice nseg has no candidates
+        cnt[u] = sm.segoff[min(sl + 1, nseg)] - sm.segoff[sl];
+      }
+      const uint2* gs = base + (int64_t)sb * P.cap_w;
+      uint2 first[kGatherB];
+#pragma unroll
+      for (int u = 0; u < kGatherB; ++u) {
+        first[u] = make_uint2(0, 0);
+        if (j < cnt[u]) first[u] = gs[(int64_t)u * kRW * P.cap_w + j];
+      }
+      per_batch(sb, cnt, first, gs);
+    }
+  };
+  // f(jj, w, ok) over a slice's entries in id order, 64 per (wave-uniform) call; entries
+  // past the first 64 load 8 rounds at a time
+  auto slice_chunks = [&](const uint2* gsl, uint32_t cnt, uint2 first, auto f) {
+    f(j, first, j < cnt);
+    for (uint32_t j0 = 64; j0 < cnt; j0 += 64 * 8) {
+      uint2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t jj = j0 + 64 * u + j;
+        v[u] = jj < cnt ? gsl[jj] : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + 64 * u < cnt) f(j0 + 64 * u + j, v[u], j0 + 64 * u + j < cnt);
+      }
+    }
+  };
+  const Digit g = first_digit(kmax, cmin);
+  if (g.lo == 0) {
+    // every candidate key is equal: the first ke candidates in id order are the top ke
+    *lo_key = kmax;
+    const uint32_t nk = min(sm.segoff[nseg], ke);
+    for (int sl = wave(); sl < nseg; sl += kRW) {
+      const uint32_t o = sm.segoff[sl];
+      if (o >= nk) break;   // slices are in id order
+      const uint32_t c = min(sm.segoff[sl + 1], nk) - o;
+      const uint2* gsl = base + (int64_t)sl * P.cap_w;
+      slice_chunks(gsl, c, j < c ? gsl[j] : make_uint2(0, 0), [&](uint32_t jj, uint2 w, bool ok) {
+        if (ok) {
+          sm.ckey[o + jj] = w.x;
+          sm.cidx[o + jj] = w.y;
+        }
+      });
+    }
+    bar();
+    return nk;
+  }
+  // pass 1: first-digit histogram of every candidate
+  batches([&](int, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
+#pragma unroll
+    for (int u = 0; u < kGatherB; ++u) {
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+        if (ok) hist_add(sm.hist, (w.x >> g.sh) & g.dm);
+      });
+    }
+  });
+  bar();
+  search_count(sm, ke);
+  if (sm.res[1] + sm.res[2] > (uint32_t)kLdsCand) return 0u;
+  const uint32_t thr_key = shl((g.prefix << (g.lo - g.sh)) | sm.res[0], g.sh);
+  *lo_key = thr_key;
+  // pass 2: per-slice counts of the kept candidates, in sm.kkey (not yet in use)
+  batches([&](int sb, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
+#pragma unroll
+    for (int u = 0; u < kGatherB; ++u) {
+      uint32_t c = 0;
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+        c += (uint32_t)__popcll(__ballot(ok && w.x >= thr_key));
+      });
+      const int sl = sb + u * kRW;
+      if (j == 0 && sl < nseg) sm.kkey[sl] = c;
+    }
+  });
+  bar();
+  uint32_t nf;
+  {
+    const int s0 = kSegPT * (int)threadIdx.x;
+    uint32_t cs[kSegPT], csum = 0;
+#pragma unroll
+    for (int q = 0; q < kSegPT; ++q) {
+      cs[q] = s0 + q < nseg ? sm.kkey[s0 + q] : 0u;
+      csum += cs[q];
+    }
+    uint32_t off = block_excl_scan<kRW>(csum, sm.red, nf);   // barrier before the writes
+#pragma unroll
+    for (int q = 0; q < kSegPT; ++q) {
+      if (s0 + q < nseg) sm.kkey[s0 + q] = off;
+      off += cs[q];
+    }
+  }
+  if (nf > (uint32_t)kLdsCand) return 0u;   // uniform: every thread holds the scan total
+  bar();
+  // pass 3: the kept candidates into LDS at their id-ordered positions
+  batches([&](int sb, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
+#pragma unroll
+    for (int u = 0; u < kGatherB; ++u) {
+      uint32_t pos = sm.kkey[min(sb + u * kRW, nseg - 1)];
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+        const bool keep = ok && w.x >= thr_key;
+        const uint64_t bal = __ballot(keep);
+        const uint32_t at = pos + mbcnt(bal);
+        if (keep && at < nf) {
+          sm.ckey[at] = w.x;
+          sm.cidx[at] = w.y;
+        }
+        pos += (uint32_t)__popcll(bal);
+      });
+    }
+  });
+  bar();
+  return nf;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   __shared__ Smem sm;
@@ -1437,7 +1586,9 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     return;
   }
 
-  if (path == kPathCand && nseg <= kMaxSeg && !P.force_exact && (flags & kFlagOverflow) == 0) {
+  // the smallest key the exact path must consider (a lower bound of the row's k-th key)
+  uint32_t kfloor = kKeyNegInf;
+  if (path == kPathCand && nseg <= kMaxSeg) {
     const uint32_t ke = (uint32_t)rp.k_eff;
     // exclusive prefix of the slice counts (kSegPT consecutive slices per thread): the
     // candidates' flat, id-ordered index space
@@ -1456,12 +1607,19 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       off += cs[q];
     }
     if (threadIdx.x == 0) sm.segoff[nseg] = total;
-    if (total >= ke && total <= (uint32_t)kLdsCand) {
+    // Wave w published the elements >= its threshold (at most the cap of them when it
+    // overflowed): at least `total` elements are >= cmin, so the k-th key is >= cmin (used
+    // only when a top-k select runs, k < V).
+    if (total >= ke && ke < (uint32_t)P.V) kfloor = cmin;
+    const bool fast = !P.force_exact && (flags & kFlagOverflow) == 0 && total >= ke;
+    uint32_t ntot = 0, lo_key = cmin;
+    bool pre = false;
+    if (fast && total <= (uint32_t)kLdsCand) {
       bar();
       // The top-k select's first pass is counted while the candidates are written to LDS:
       // every candidate key lies in [cmin, kmax], so its digit needs no prefix test.
       const Digit g0 = first_digit(kmax, cmin);
-      const bool pre = total > ke && g0.lo > 0;
+      pre = total > ke && g0.lo > 0;
       auto put = [&](uint32_t f, uint2 v) {
         sm.ckey[f] = v.x;
         sm.cidx[f] = v.y;
@@ -1496,17 +1654,35 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           if (more) {   // wave-uniform: some slice of the batch holds more than 64 candidates
 #pragma unroll
             for (int u = 0; u < kGatherB; ++u) {
-              for (uint32_t jj = 64u + j; jj < cnt[u]; jj += 64u) put(o[u] + jj, gs[(int64_t)u * kRW * P.cap_w + jj]);
+              for (uint32_t j0 = 64u; j0 < cnt[u]; j0 += 256u) {   // 4 loads in flight per lane
+                uint2 w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t jj = j0 + 64u * e + j;
+                  w[e] = jj < cnt[u] ? gs[(int64_t)u * kRW * P.cap_w + jj] : make_uint2(0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t jj = j0 + 64u * e + j;
+                  if (jj < cnt[u]) put(o[u] + jj, w[e]);
+                }
+              }
             }
           }
         }
       }
       bar();
-      auto vis = [&](auto f) { lds_for(sm.ckey, sm.cidx, total, f); };
+      ntot = total;
+    } else if (fast) {
+      bar();
+      ntot = gather_filtered(P, r, nseg, ke, kmax, cmin, sm, &lo_key);
+    }
+    if (ntot) {
+      auto vis = [&](auto f) { lds_for(sm.ckey, sm.cidx, ntot, f); };
       Sel sk = sel_all();
-      uint32_t min_sel = cmin;
-      if (total > ke) {
-        sk = select_topk(vis, ke, total, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm, pre);
+      uint32_t min_sel = lo_key;
+      if (ntot > ke) {
+        sk = select_topk(vis, ke, ntot, kmax, lo_key, 0u, (uint32_t)(P.V - 1), sm, pre);
         min_sel = shl(sk.prefix, sk.lo);
       }
       // Certification: every element of the row with a key >= the smallest selected key
@@ -1516,19 +1692,18 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
           const uint32_t kmx = (uint32_t)P.k_max;
           uint32_t run = 0;
-          emit_ordered<4>(total, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
+          emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
                           [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
                           [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
           for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
           return;
         }
-        finish_cand<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, total, sk, sm);
+        finish_cand<MODE>(P, rp, r, kmax, max(lo_key, min_sel), seed, ntot, sk, sm);
         return;
       }
     }
   }
-  // the smallest possible key of a non-NaN element
-  row_stream<MODE>(P, rp, r, kmax, kKeyNegInf, seed, sm);
+  row_stream<MODE>(P, rp, r, kmax, kfloor, seed, sm);
 }
 
 __global__ void ts_fill_kernel(uint32_t* p, size_t n_words) {
