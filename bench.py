@@ -84,6 +84,7 @@ def cpu_baseline(batch, budget_s: float = 12.0):
 # data from HBM: R * bytes >= 512 MB where it fits, the MALL being 256 MB).
 OTHER_CONFIGS = {
     "tiny": ("tiny", "sample", 4),
+    "decode_topp_only": ("decode_topp_only", "sample", 16),
     "heavy": ("heavy", "sample", 16),
     "tie_stress": ("tie_stress", "sample", 8),
     "indexer_rows": ("indexer_rows", "topk", 32),

@@ -248,6 +248,19 @@ def test_topp_decode_rows_sampled():
     check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "decode")
 
 
+def test_topp_and_sample_decode_topk_off_sampled():
+    # top-p over whole 151936-element rows (top-k disabled): the row-streaming path with its
+    # boundary bin continued in LDS and the Gumbel draws compacted to the kept set
+    b = wl.decode_topp_only()
+    banner("topp + sample decode with k off 64x151936 (8 rows checked)")
+    kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
+    tok, st2 = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    sel = [0, 2, 11, 16, 33, 47, 56, 59]
+    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "topk-off")
+    check_samples(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], b.seeds[sel], tok[sel], st2[sel], kept[sel],
+                  "topk-off", row_ids=sel)
+
+
 def test_topp_tie_stress_sampled():
     b = wl.tie_stress()
     banner("topp tie stress 128x128256 (12 rows incl. the all-equal row)")

@@ -143,8 +143,7 @@ struct Smem {
   uint32_t ckey[kLdsCand];     // candidates (id order), keys and ids in separate arrays
   uint32_t cidx[kLdsCand];
   alignas(16) uint32_t hist[kDBins];   // count histogram; each thread reads and re-zeroes its own bins
-  alignas(16) uint64_t mhi[kDBins];    // mass histogram (fixed-point halves)
-  alignas(16) uint64_t mlo[kDBins];
+  alignas(16) uint64_t mhi[kDBins];    // mass histogram (fixed-point sums)
   uint32_t kkey[kFastK];       // the kept set P, compacted for the Gumbel draws
   uint32_t kidx[kFastK];
   uint32_t segoff[kMaxSeg + 1];
@@ -264,77 +263,55 @@ __device__ __forceinline__ void search_count(Smem& sm, uint32_t need) {
   bar();
 }
 
-// Mass: the highest bin b with ma + (mass in bins >= b) >= target, masses exact fixed-point
-// sums compared after conversion to binary64. TWO: two 64-bit words per mass (hi, lo; the
-// row-streaming path, where K can be the whole row); otherwise one word (the candidate path,
-// |K| <= kFastK). Writes res[0] = b, res[1] = count above, res[2] = count in b,
-// res64[0..1] = ma + mass above b, res64[2..3] = mass of b (lo words 0 when !TWO).
-template <bool TWO>
-__device__ __forceinline__ void search_mass(Smem& sm, double target, uint64_t target_fx, uint64_t ma_hi,
-                                            uint64_t ma_lo, int S) {
+// Mass: the highest bin b with ma + (mass in bins >= b) >= target_fx, masses being exact
+// fixed-point sums (one 64-bit word floor(w * 2^S) per weight). Writes res[0] = b,
+// res[1] = count above b, res[2] = count in b, res64[0] = ma + mass above b, res64[1] = mass
+// of b. The caller guarantees that ma plus the whole histogram reaches the target.
+__device__ __forceinline__ void search_mass(Smem& sm, uint64_t target_fx, uint64_t ma) {
   const int t = threadIdx.x;
   uint32_t c[kBPT];
-  uint64_t mh[kBPT], ml[kBPT];
+  uint64_t mh[kBPT];
   take_bins(sm.hist, t, c);
 #pragma unroll
-  for (int j = 0; j < kBPT; ++j) {
-    mh[j] = sm.mhi[kBPT * t + j];
-    ml[j] = TWO ? sm.mlo[kBPT * t + j] : 0ull;
-  }
+  for (int j = 0; j < kBPT; ++j) mh[j] = sm.mhi[kBPT * t + j];
 #pragma unroll
-  for (int j = 0; j < kBPT; ++j) {
-    sm.mhi[kBPT * t + j] = 0;
-    if (TWO) sm.mlo[kBPT * t + j] = 0;
-  }
+  for (int j = 0; j < kBPT; ++j) sm.mhi[kBPT * t + j] = 0;
   uint32_t lc = 0;
-  uint64_t lh = 0, ll = 0;
+  uint64_t lh = 0;
 #pragma unroll
   for (int j = 0; j < kBPT; ++j) {
     lc += c[j];
     lh += mh[j];
-    ll += ml[j];
   }
   const uint32_t sc = wave_incl_suffix(lc);
   const uint64_t sh = wave_incl_suffix64(lh);
-  const uint64_t sl = TWO ? wave_incl_suffix64(ll) : 0ull;
   if (lane() == 0) {
     sm.red[wave()] = sc;
     sm.red64[wave()] = sh;
-    if (TWO) sm.red64[kRW + wave()] = sl;
   }
   bar();
   uint32_t ac = 0;
-  uint64_t ah = 0, al = 0;
+  uint64_t ah = 0;
 #pragma unroll
   for (int w = 0; w < kRW; ++w) {
     const bool up = w > wave();
     ac += up ? sm.red[w] : 0u;
     ah += up ? sm.red64[w] : 0ull;
-    if (TWO) al += up ? sm.red64[kRW + w] : 0ull;
   }
-  // reaches(h, l): the mass (h, l) is >= the target -- in binary64 for two words, exactly in
-  // fixed point for one (target_fx = ceil(p * Z) in the same units)
-  auto reaches = [&](uint64_t h, uint64_t l) { return TWO ? mass_to_double(h, l, S) >= target : h >= target_fx; };
   uint32_t xc = ac + sc - lc;
-  uint64_t xh = ma_hi + ah + sh - lh;
-  uint64_t xl = TWO ? ma_lo + al + sl - ll : 0ull;
-  const bool below = !reaches(xh, xl);
-  const bool reach = reaches(xh + lh, xl + ll);
-  if (below && reach) {
+  uint64_t xh = ma + ah + sh - lh;
+  if (xh < target_fx && xh + lh >= target_fx) {
     int j = kBPT - 1;
     for (; j > 0; --j) {
-      if (reaches(xh + mh[j], xl + ml[j])) break;
+      if (xh + mh[j] >= target_fx) break;
       xh += mh[j];
-      xl += ml[j];
       xc += c[j];
     }
     sm.res[0] = kBPT * t + j;
     sm.res[1] = xc;
     sm.res[2] = c[j];
     sm.res64[0] = xh;
-    sm.res64[1] = xl;
-    sm.res64[2] = mh[j];
-    sm.res64[3] = ml[j];
+    sm.res64[1] = mh[j];
   }
   bar();
 }
@@ -533,23 +510,53 @@ __device__ __forceinline__ Sel select_topk(const Vis& vis, uint32_t need, uint32
 }
 
 // ------------------------------------------------------------------ mass select (top-p)
-// Smallest prefix of the row ordering whose exact fixed-point mass reaches `target`
+// Visit the items [0, n) of an LDS (key, id) array pair: kVisU per thread per round, all LDS
+// reads of a round issued before any item is used. f(rk, idx) is called for each item.
+template <class F>
+__device__ __forceinline__ void lds_for(const uint32_t* ka, const uint32_t* ia, uint32_t n, F f) {
+  for (uint32_t base = threadIdx.x; base < n; base += kRT * kVisU) {
+    uint32_t k[kVisU], x[kVisU];
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      const uint32_t i = min(base + u * kRT, n - 1);   // clamped: in bounds, result unused past n
+      k[u] = ka[i];
+      x[u] = ia[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kVisU; ++u) {
+      if (base + u * kRT < n) f(k[u], x[u]);
+    }
+  }
+}
+
+// Visitor over LDS arrays (a fixed type, so that a select can continue on a list it built).
+struct LdsVis {
+  const uint32_t* ka;
+  const uint32_t* ia;
+  uint32_t n;
+  template <class F>
+  __device__ __forceinline__ void operator()(F f) const { lds_for(ka, ia, n, f); }
+};
+
+// Smallest prefix of the row ordering whose exact fixed-point mass reaches `target_fx`
 // ([TOPP] "Independent binary64 numerical reference", steps 4-5, with the predicate kept in
 // probability space, [TOPP] "Source basis"). kvis(f) calls f(rk, idx) for this thread's items
 // of K; wmass(rk) returns the fixed-point weight of a key (computed only for items still in
 // play). Result: Sel of the kept set P (a canonical prefix) and |P| in `kept`. Both histograms
 // are zero on entry and on return. With `prebuilt`, the caller has already accumulated the
 // first pass (digit first_digit(hi_key, lo_key), counts and masses) and passed a barrier; it
-// may do so only when hi_key != lo_key.
-template <bool TWO, class KVis, class WMass>
-__device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, double target, uint64_t target_fx, int S,
+// may do so only when hi_key != lo_key. ma0 and n_above0 are the mass and the count of items
+// above the ones in play. COLLECT (the row-streaming path, whose LDS candidate arrays are
+// free): a boundary bin that fits in LDS is copied there and the select continues on it.
+template <bool COLLECT = false, class KVis, class WMass>
+__device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, uint64_t target_fx,
                                            uint32_t n_in_play, uint32_t hi_key, uint32_t lo_key,
                                            uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept,
-                                           bool prebuilt = false) {
+                                           bool prebuilt = false, uint64_t ma0 = 0, uint32_t n_above0 = 0) {
   int lo = (hi_key == lo_key) ? 0 : 32 - __clz((int)(hi_key ^ lo_key));
   uint32_t prefix = shr(hi_key, lo);
-  uint32_t n_above = 0, tie_cnt = n_in_play;
-  uint64_t ma_hi = 0, ma_lo = 0, bin_hi = 0, bin_lo = 0;
+  uint32_t n_above = n_above0, tie_cnt = n_in_play;
+  uint64_t ma = ma0, bin_m = 0;
   bool single = false, ran = false, counted = prebuilt;
   while (lo > 0) {
     const int d = min(kDBits, lo);
@@ -562,27 +569,23 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
       kvis([&](uint32_t rk, uint32_t) {
         if (shr(rk, lo_now) == pre) {
           const uint32_t b = (rk >> sh) & dm;
-          const Mass q = wmass(rk);
-          atomicAdd(&sm.hist[b], 1u);
-          atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q.hi);
-          if (TWO) atomicAdd((unsigned long long*)&sm.mlo[b], (unsigned long long)q.lo);
+          hist_add(sm.hist, b);
+          atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)wmass(rk));
         }
       });
       bar();
     }
     counted = false;
-    search_mass<TWO>(sm, target, target_fx, ma_hi, ma_lo, S);
+    search_mass(sm, target_fx, ma);
     const uint32_t bin = sm.res[0];
     n_above += sm.res[1];
     tie_cnt = sm.res[2];
-    ma_hi = sm.res64[0];
-    ma_lo = sm.res64[1];
-    bin_hi = sm.res64[2];
-    bin_lo = sm.res64[3];
+    ma = sm.res64[0];
+    bin_m = sm.res64[1];
     prefix = (prefix << d) | bin;
     lo = sh;
     if (tie_cnt == 1) { single = true; break; }
-    if (!TWO && tie_cnt <= kSmallBin) {
+    if (tie_cnt <= kSmallBin) {
       // Rank the bin's items, lay their masses out in row order, and cut at the first
       // prefix whose mass (above the bin plus the prefix) reaches the target.
       collect_bin(kvis, prefix, lo, sm);
@@ -591,10 +594,10 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
         const uint32_t c = tie_cnt;
         const uint32_t rank = bin_rank(c, k, x, sm);
         const bool in = (uint32_t)lane() < c;
-        if (in) sm.bmass[rank] = wmass(k).hi;
+        if (in) sm.bmass[rank] = wmass(k);
         wave_lds_sync();
         const uint64_t cum = wave_incl_scan64(in ? sm.bmass[lane()] : 0ull);
-        const uint64_t hit = __ballot(in && ma_hi + cum >= target_fx);
+        const uint64_t hit = __ballot(in && ma + cum >= target_fx);
         const uint32_t j = hit ? (uint32_t)__builtin_ctzll(hit) : c - 1u;   // the bin reaches it
         if (in && rank == j) {
           sm.bres[0] = k;
@@ -609,36 +612,37 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
       kept = n_above + sm.bres[2];
       return Sel{sm.bres[0], 0, sm.bres[1]};
     }
+    if constexpr (COLLECT) {
+      if (lo > 0 && tie_cnt <= (uint32_t)kLdsCand) {
+        const uint32_t pre2 = prefix;
+        const int lo2 = lo;
+        kvis([&](uint32_t rk, uint32_t idx) {
+          if (shr(rk, lo2) == pre2) {
+            const uint32_t p = atomicAdd(&sm.bcount, 1u);
+            if (p < (uint32_t)kLdsCand) {
+              sm.ckey[p] = rk;
+              sm.cidx[p] = idx;
+            }
+          }
+        });
+        bar();
+        if (threadIdx.x == 0) sm.bcount = 0;   // read by no one before the next barrier
+        const uint32_t base_key = shl(prefix, lo);
+        return select_mass<false>(LdsVis{sm.ckey, sm.cidx, tie_cnt}, wmass, target_fx, tie_cnt,
+                                  base_key | ((1u << lo) - 1u), base_key, idx_lo, idx_hi, sm, kept, false,
+                                  ma, n_above);
+      }
+    }
   }
   uint32_t take = 1;
   if (!single && tie_cnt > 1) {
     // The boundary key is shared by tie_cnt items of identical weight q (same key, same
-    // fp32 logit, same binary64 weight): take the fewest of them, lowest ids first, that
-    // bring the mass above to the target.
-    uint64_t qh, ql;
-    if (ran) {
-      qh = bin_hi / tie_cnt;
-      ql = bin_lo / tie_cnt;
-    } else {  // every in-play key is equal and no pass ran
-      const Mass q1 = wmass(prefix);
-      qh = q1.hi;
-      ql = q1.lo;
-    }
-    auto reaches = [&](uint64_t h, uint64_t l) { return TWO ? mass_to_double(h, l, S) >= target : h >= target_fx; };
-    uint32_t t;
-    if (TWO) {
-      const double q = mass_to_double(qh, ql, S);
-      const double ma = mass_to_double(ma_hi, ma_lo, S);
-      const double j = q > 0.0 ? ceil((target - ma) / q) : (double)tie_cnt;
-      t = (uint32_t)fmin(fmax(j, 1.0), (double)tie_cnt);
-    } else {   // exact: the fewest t with ma + t * q >= target_fx
-      const uint64_t rest = target_fx > ma_hi ? target_fx - ma_hi : 0ull;
-      const uint64_t j = qh > 0 ? (rest + qh - 1) / qh : (uint64_t)tie_cnt;
-      t = (uint32_t)min(max(j, (uint64_t)1), (uint64_t)tie_cnt);
-    }
-    while (t > 1 && reaches(ma_hi + qh * (t - 1), ma_lo + ql * (t - 1))) --t;
-    while (t < tie_cnt && !reaches(ma_hi + qh * t, ma_lo + ql * t)) ++t;
-    take = t;
+    // fp32 logit, same weight): take the fewest of them, lowest ids first, that bring the
+    // mass to the target.
+    const uint64_t q = ran ? bin_m / tie_cnt : wmass(prefix);
+    const uint64_t rest = target_fx > ma ? target_fx - ma : 0ull;
+    const uint64_t j = q > 0 ? (rest + q - 1) / q : (uint64_t)tie_cnt;
+    take = (uint32_t)min(max(j, (uint64_t)1), (uint64_t)tie_cnt);
   }
   Sel s{prefix, lo, 0xFFFFFFFFu};
   if (take < tie_cnt) {
@@ -660,8 +664,29 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
 
 // ------------------------------------------------------------------ misc helpers
 
-__device__ __forceinline__ double weight_of(uint32_t key, float m, float t) {
-  return exp(((double)key2f(key) - (double)m) / (double)t);
+constexpr double kLog2e = 1.4426950408889634;   // log2(e)
+
+// Unnormalized weight exp((x - m) / T) of a key, about 1.5e-7 relative: the base-2 exponent
+// z = (x - m) * log2(e) / T is formed in binary64 (x - m exact, c2 = log2(e) / T rounded
+// once), split into integer and fraction, and only 2^fraction is evaluated in fp32.
+// -inf logits (and weights below 2^-200) give 0.
+__device__ __forceinline__ float weight32(uint32_t key, float m, double c2) {
+  const double z = ((double)key2f(key) - (double)m) * c2;   // <= 0
+  if (!(z > -200.0)) return 0.0f;
+  const double n = floor(z);
+  return ldexpf(exp2f((float)(z - n)), (int)n);
+}
+
+// ceil(p * Z) for p = fp32 in (0, 1) and a fixed-point total Z: with p = mant * 2^-psh
+// (mant < 2^24) the product is exact in 128 bits.
+__device__ __forceinline__ uint64_t topp_target(float p, uint64_t z) {
+  int pe;
+  const float pf = frexpf(p, &pe);                          // p = pf * 2^pe, pf in [0.5, 1)
+  const uint64_t mant = (uint64_t)ldexpf(pf, 24);
+  const int psh = 24 - pe;                                  // > 24 since p < 1
+  const unsigned __int128 prod = (unsigned __int128)mant * z;
+  return psh >= 128 ? (prod != 0 ? 1ull : 0ull)
+                    : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
 }
 
 __device__ __forceinline__ float gumbel_score(uint32_t key, uint32_t idx, float m, float t,
@@ -706,24 +731,6 @@ __device__ __forceinline__ void emit_ordered(uint32_t n, const Get& get, const M
   }
 }
 
-// Visit the items [0, n) of an LDS (key, id) array pair: kVisU per thread per round, all LDS
-// reads of a round issued before any item is used. f(rk, idx) is called for each item.
-template <class F>
-__device__ __forceinline__ void lds_for(const uint32_t* ka, const uint32_t* ia, uint32_t n, F f) {
-  for (uint32_t base = threadIdx.x; base < n; base += kRT * kVisU) {
-    uint32_t k[kVisU], x[kVisU];
-#pragma unroll
-    for (int u = 0; u < kVisU; ++u) {
-      const uint32_t i = min(base + u * kRT, n - 1);   // clamped: in bounds, result unused past n
-      k[u] = ka[i];
-      x[u] = ia[i];
-    }
-#pragma unroll
-    for (int u = 0; u < kVisU; ++u) {
-      if (base + u * kRT < n) f(k[u], x[u]);
-    }
-  }
-}
 
 // lds_for over K = (kkey, kidx)[0, n) that also passes each item's position: f(i, key, id).
 template <class F>
@@ -1179,10 +1186,11 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
   uint32_t kept = nk;
   if (rp.p != 1.0f) {
     // One visit of K computes every weight once: Z, and the counts and masses of the mass
-    // select's first pass. |K| <= kFastK, so one 64-bit word floor(w * 2^S) per weight sums
-    // exactly (S = 63 - bitlen(|K|) >= 51; truncation costs < |K| * 2^-S of Z).
+    // select's first pass. One 64-bit word floor(w * 2^S) per weight sums exactly
+    // (S = 63 - bitlen(|K|); truncation costs < |K| * 2^-S of Z >= 1).
     const int S = 63 - bitlen(nk);
-    auto wmass = [&](uint32_t rk) { return Mass{mass1_of(weight_of(rk, m, t), S), 0ull}; };
+    const double c2 = kLog2e / (double)t;
+    auto wmass = [&](uint32_t rk) { return mass1_of((double)weight32(rk, m, c2), S); };
     const Digit g = first_digit(kmax, klo);
     const bool pre = g.lo > 0;
     // When sampling, the same visit draws every item's Gumbel score into gsc[i] (the
@@ -1201,7 +1209,7 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
       for (int u = 0; u < kVisU; ++u) {
         const uint32_t i = base + u * kRT;
         if (i < nk) {
-          const uint64_t q = mass1_of(weight_of(kr[u], m, t), S);
+          const uint64_t q = wmass(kr[u]);
           zh += q;
           if (pre) {
             const uint32_t b = (kr[u] >> g.sh) & g.dm;
@@ -1214,16 +1222,9 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
     }
     block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics and stores
     // [TOPP] reference steps 4-5 in exact fixed point: keep the shortest prefix whose mass is
-    // >= p * Z, i.e. >= ceil(p * Z) since masses are integers; p = mant * 2^-sh (mant < 2^24).
-    int pe;
-    const float pf = frexpf(rp.p, &pe);                       // rp.p = pf * 2^pe, pf in [0.5, 1)
-    const uint64_t mant = (uint64_t)ldexpf(pf, 24);
-    const int psh = 24 - pe;                                  // > 24 since p < 1
-    const unsigned __int128 prod = (unsigned __int128)mant * zh;
-    const uint64_t target_fx = psh >= 128 ? (prod != 0 ? 1ull : 0ull)
-                                          : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
-    const double target = (double)rp.p * ldexp((double)zh, -S);   // unused by the one-word search
-    sp = select_mass<false>(kvis, wmass, target, target_fx, S, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
+    // >= p * Z, i.e. >= ceil(p * Z) since masses are integers.
+    const uint64_t target_fx = topp_target(rp.p, zh);
+    sp = select_mass(kvis, wmass, target_fx, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -1265,15 +1266,20 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   const uint32_t V = (uint32_t)P.V;
   const bool al4 = ((uintptr_t)row & 15u) == 0;
   auto rvis = [&](auto f) {
-    if (al4) {   // 8 float4 loads in flight per thread per round
+    if (al4) {   // 8 float4 loads per thread per round; the next round loads during this one
       const uint32_t nq = V >> 2;
+      const uint4* rq = reinterpret_cast<const uint4*>(row);
+      uint4 v[8], nx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = u * kRT + threadIdx.x;
+        v[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
+      }
       for (uint32_t base = 0; base < nq; base += kRT * 8) {
-        uint4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const uint32_t q = base + u * kRT + threadIdx.x;
-          v[u] = make_uint4(0, 0, 0, 0);
-          if (q < nq) v[u] = reinterpret_cast<const uint4*>(row)[q];
+          const uint32_t q = base + kRT * 8 + u * kRT + threadIdx.x;
+          nx[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -1285,6 +1291,8 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
             f(f2key(__uint_as_float(v[u].w)), 4 * q + 3);
           }
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = nx[u];
       }
       for (uint32_t i = 4 * nq + threadIdx.x; i < V; i += kRT) f(f2key(row[i]), i);
     } else {
@@ -1327,18 +1335,26 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   Sel sp = sel_all();
   uint32_t kept = ke;
   if (rp.p != 1.0f) {
+    // One visit of K: Z and the mass select's first pass (counts and masses of the first
+    // digit over [klo, kmax], where every key of K lies).
     const int S = 63 - bitlen(ke);
+    const double c2 = kLog2e / (double)t;
+    auto wmass = [&](uint32_t rk) { return mass1_of((double)weight32(rk, m, c2), S); };
+    const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
+    const Digit g = first_digit(kmax, klo);
+    const bool pre = g.lo > 0;
     uint64_t zh = 0, zl = 0;
     kvis([&](uint32_t rk, uint32_t) {
-      const Mass q = mass_of(weight_of(rk, m, t), S);
-      zh += q.hi;
-      zl += q.lo;
+      const uint64_t q = wmass(rk);
+      zh += q;
+      if (pre) {
+        const uint32_t b = (rk >> g.sh) & g.dm;
+        hist_add(sm.hist, b);
+        atomicAdd((unsigned long long*)&sm.mhi[b], (unsigned long long)q);
+      }
     });
-    block_sum2_u64<kRW>(zh, zl, sm.red64);
-    const double target = (double)rp.p * mass_to_double(zh, zl, S);
-    const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
-    sp = select_mass<true>(kvis, [&](uint32_t rk) { return mass_of(weight_of(rk, m, t), S); }, target, 0ull, S, ke,
-                     kmax, klo, 0u, V - 1, sm, kept);
+    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics
+    sp = select_mass<true>(kvis, wmass, topp_target(rp.p, zh), ke, kmax, klo, 0u, V - 1, sm, kept, pre);
   }
   if (MODE == kModeTopp) {
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
@@ -1349,15 +1365,73 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       });
     }
   } else {
+    // Gumbel-max over P. Per slab of kLdsCand row elements the members of P are compacted
+    // into LDS first, so that noise is drawn only for them (members are scattered: drawing
+    // in place would run the generator in nearly every wave for every element).
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    constexpr int kPer = kLdsCand / kRT;
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
-    kvis([&](uint32_t rk, uint32_t idx) {
-      if (sel_member(sp, rk, idx)) {
-        const float sc = gumbel_score(rk, idx, m, t, (uint32_t)r, k0, k1);
-        if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
+    auto load = [&](uint32_t s0, uint32_t (&key)[kPer]) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const uint32_t i = s0 + (uint32_t)(u * kRT) + threadIdx.x;
+        key[u] = i < V ? __float_as_uint(row[i]) : 0u;
       }
-    });
+    };
+    uint32_t cur[kPer], nxt[kPer];
+    load(0, cur);
+    for (uint32_t s0 = 0; s0 < V; s0 += (uint32_t)kLdsCand) {
+      load(s0 + (uint32_t)kLdsCand, nxt);   // the next slab loads while this one is processed
+      uint64_t bal[kPer];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const uint32_t i = s0 + (uint32_t)(u * kRT) + threadIdx.x;
+        cur[u] = f2key(__uint_as_float(cur[u]));
+        bal[u] = __ballot(i < V && sel_member(sk, cur[u], i) && sel_member(sp, cur[u], i));
+        tot += (uint32_t)__popcll(bal[u]);
+      }
+      if (tot) {   // wave-uniform: one reservation per wave and slab
+        uint32_t wbase = 0;
+        if (lane() == 0) wbase = atomicAdd(&sm.bcount, tot);
+        wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          if ((bal[u] >> lane()) & 1ull) {
+            const uint32_t at = wbase + mbcnt(bal[u]);   // < kLdsCand: one slab's members
+            sm.ckey[at] = cur[u];
+            sm.cidx[at] = s0 + (uint32_t)(u * kRT) + threadIdx.x;
+          }
+          wbase += (uint32_t)__popcll(bal[u]);
+        }
+      }
+      bar();
+      const uint32_t nq = sm.bcount;
+      // four independent draws per thread per step
+      for (uint32_t q0 = threadIdx.x; q0 < nq; q0 += 4 * kRT) {
+        float sc[4];
+        uint32_t id[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t q = min(q0 + (uint32_t)(e * kRT), nq - 1u);
+          id[e] = sm.cidx[q];
+          sc[e] = gumbel_score(sm.ckey[q], id[e], m, t, (uint32_t)r, k0, k1);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (q0 + (uint32_t)(e * kRT) < nq && (sc[e] > bs || (sc[e] == bs && (int32_t)id[e] < bi))) {
+            bs = sc[e];
+            bi = (int32_t)id[e];
+          }
+        }
+      }
+      bar();
+      if (threadIdx.x == 0) sm.bcount = 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) cur[u] = nxt[u];
+      bar();
+    }
     const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
     if (threadIdx.x == 0) P.out_token[r] = tok;
   }
@@ -1521,7 +1595,6 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   for (int i = threadIdx.x; i < kDBins / 4; i += kRT) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kDBins / 2; i += kRT) {
     reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
-    reinterpret_cast<uint4*>(sm.mlo)[i] = make_uint4(0, 0, 0, 0);
   }
   // kmax, thr_max: maxima; cmin: every candidate key is >= the smallest threshold
   block_reduce4<kRW>(kmax, thr_max, cmin, flags, sm.red);

@@ -263,24 +263,9 @@ __device__ __forceinline__ float uniform_from_word(uint32_t w) {
 __device__ __forceinline__ float gumbel_from_uniform(float u) { return -logf(-log1pf(-u)); }
 
 // ---------------------------------------------------------------- fixed-point mass
-// Probability mass is summed exactly as two unsigned 64-bit integer parts so that
-// histograms and totals do not depend on the order of the additions: a weight w in [0,1]
-// is represented as floor(w * 2^(2S)) = hi * 2^S + lo with 0 <= lo < 2^S, where S is chosen
-// per row so that n weights cannot overflow 64 bits in either part (S = 63 - bitlen(n)).
-struct Mass {
-  uint64_t hi, lo;
-};
-__device__ __forceinline__ Mass mass_of(double w, int s) {
-  const double t = ldexp(w, s);                 // exact scaling
-  const uint64_t hi = (uint64_t)t;              // truncation; t < 2^S + 1
-  const double f = t - (double)hi;              // exact fractional part
-  const uint64_t lo = (uint64_t)ldexp(f, s);    // exact truncation
-  return Mass{hi, lo};
-}
-__device__ __forceinline__ double mass_to_double(uint64_t hi, uint64_t lo, int s) {
-  return ldexp((double)hi, -s) + ldexp((double)lo, -2 * s);
-}
-// One-word form for sets of at most 2^(63-S) weights: floor(w * 2^S), exact to truncation.
+// Probability mass is summed exactly in unsigned 64-bit fixed point so that histograms and
+// totals do not depend on the order of the additions: a weight w in [0, 1] counts as
+// floor(w * 2^S), S chosen per row so that n weights cannot overflow (S = 63 - bitlen(n)).
 __device__ __forceinline__ uint64_t mass1_of(double w, int s) { return (uint64_t)ldexp(w, s); }
 
 }  // namespace tsd

@@ -11,6 +11,7 @@ and prompts the pages measured on):
 * ``decode``      64 x 151936 logits 2.5*N(0,1) with 20 distinct head tokens raised by
                   +8 per row; k ~ U{1..1024}, p ~ U[0.5,1), T ~ U[0.5,1.5). V=151936 is the
                   vocabulary in RL-Kernel issue #332 ("Summary").
+* ``decode_topp_only``  the decode rows with top-k disabled (k = V).
 * ``heavy``       256 identical rows of V=32000, logits = log(counts), counts in {1,2,3}
                   and counts[0] = round(e^18) (vLLM PR #45996 summary, "key source
                   excerpts": the heavy-tailed fidelity test); k off, p=1, T=1.
@@ -87,6 +88,15 @@ def decode(seed: int = 2, rows: int = 64, vocab: int = 151936) -> Batch:
     p = rng.uniform(0.5, 1.0, size=rows).astype(np.float32)
     t = rng.uniform(0.5, 1.5, size=rows).astype(np.float32)
     return Batch(logits=x, k=k, p=p, t=t, seeds=_seeds(rng, rows), k_max=1024, name="decode")
+
+
+def decode_topp_only(seed: int = 2, rows: int = 64, vocab: int = 151936) -> Batch:
+    """The decode rows with top-k disabled (k = V): top-p over the whole row."""
+    b = decode(seed, rows, vocab)
+    b.k = np.full(rows, vocab, np.int32)
+    b.k_max = vocab
+    b.name = "decode_topp_only"
+    return b
 
 
 def heavy_counts(seed: int = 3, vocab: int = 32000) -> np.ndarray:
