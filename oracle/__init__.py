@@ -23,8 +23,10 @@ from .sampler import (
     gumbel_argmax,
     gumbel_from_word,
     gumbel_noise,
+    lse_logp_row,
     neumaier_first_reach,
     row_floats,
+    sample_logp_rows,
     sample_row,
     sample_rows,
     to_f32,

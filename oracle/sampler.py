@@ -260,6 +260,41 @@ def sample_row(row, k: Optional[int], p: Optional[float], t: Optional[float],
     return SampleResult(status=STATUS_OK, token=tok, gap=gap, topp=tp)
 
 
+def lse_logp_row(row, t: Optional[float], token: int):
+    """Temperature-scaled log-sum-exp of a whole row and the log-probability of ``token``.
+
+    [LOGP] "Design: the numeric contract": m = max of the row, S = sum of exp(x - m),
+    lse = m + log S, logp = min(x_t - lse, 0); temperature enters in the epilogue
+    ([LOGP] "Contract constants", temperature), so with x/T in place of x:
+    lse = m/T + log(sum exp((x - m)/T)) and logp = min(x_t/T - lse, 0). The sum is over the
+    whole row (the model's distribution at temperature T), in binary64 with math.fsum;
+    -inf logits contribute 0. T == 0 (greedy): lse = +inf and the greedy token has logp 0.
+    """
+    x = row_floats(row)
+    tv = 1.0 if t is None else float(t)
+    if tv == 0.0:
+        return math.inf, 0.0
+    m = max(x)
+    s = math.fsum(math.exp((xi - m) / tv) for xi in x if xi != -math.inf)
+    lse = m / tv + math.log(s)
+    return lse, min(x[token] / tv - lse, 0.0)
+
+
+def sample_logp_rows(x2d, k, p, t, seeds):
+    """Batched sampling with the selected token's logprob: list of
+    (SampleResult, lse, logp), lse and logp for the oracle's own token (nan for rows
+    that are rejected)."""
+    x2d = np.asarray(x2d, dtype=np.float32)
+    out = []
+    for r, res in enumerate(sample_rows(x2d, k, p, t, seeds)):
+        if res.status != STATUS_OK:
+            out.append((res, math.nan, math.nan))
+            continue
+        lse, logp = lse_logp_row(x2d[r], _opt(t, r, to_f32), res.token)
+        out.append((res, lse, logp))
+    return out
+
+
 # --------------------------------------------------------------------------- batched
 def _opt(arr, r, cast):
     return None if arr is None else cast(arr[r])
