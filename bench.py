@@ -85,6 +85,7 @@ def cpu_baseline(batch, budget_s: float = 12.0):
 OTHER_CONFIGS = {
     "tiny": ("tiny", "sample", 4),
     "decode_topp_only": ("decode_topp_only", "sample", 16),
+    "decode_logp": ("decode", "sample_logp", 16),
     "heavy": ("heavy", "sample", 16),
     "tie_stress": ("tie_stress", "sample", 8),
     "indexer_rows": ("indexer_rows", "topk", 32),
@@ -110,7 +111,7 @@ def other_config(name, args):
     bufs = [base] + [torch.roll(base, shifts=37 * i, dims=1).contiguous() for i in range(1, rot)]
     st = torch.empty(rows, dtype=torch.int32, device=dev)
     k = torch.from_numpy(b.k).to(dev)
-    if op == "sample":
+    if op in ("sample", "sample_logp"):
         p = torch.from_numpy(b.p).to(dev)
         t = torch.from_numpy(b.t).to(dev)
         seeds = b.seeds if b.seeds is not None else wl.heavy_launch_seeds(0, rows)
@@ -122,6 +123,13 @@ def other_config(name, args):
                  ws.data_ptr(), ws.numel())
         call = lambda x, h: lib.ts_sample_rows(x, rows, vocab, vocab, *fixed, h)
         cname = "ts_sample_rows"
+        if op == "sample_logp":
+            lp = torch.empty(rows, dtype=torch.float32, device=dev)
+            ls = torch.empty(rows, dtype=torch.float32, device=dev)
+            call = lambda x, h: lib.ts_sample_rows_logp(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                                                        t.data_ptr(), s.data_ptr(), tok.data_ptr(), lp.data_ptr(),
+                                                        ls.data_ptr(), st.data_ptr(), ws.data_ptr(), ws.numel(), h)
+            cname = "ts_sample_rows_logp"
     else:
         out = torch.empty((rows, b.k_max), dtype=torch.int32, device=dev)
         nb = lib.ts_workspace_bytes(ts.TS_OP_TOPK_SELECT, rows, vocab, b.k_max)

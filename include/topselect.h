@@ -139,6 +139,26 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ts_sample_rows_logp -- ts_sample_rows plus the sampled token's log-probability under the
+ * row's temperature-scaled distribution, [LOGP] "Design: the numeric contract" with
+ * temperature applied in the epilogue ([LOGP] "Contract constants"): over the WHOLE row
+ * (before top-k / top-p), m = max x, S = sum exp((x - m)/T), lse = m/T + log S,
+ * logp = min(x_t/T - lse, 0) for the returned token t. -inf logits contribute 0 to S.
+ *   out_token   [rows] int32, identical to what ts_sample_rows returns for the same inputs.
+ *   out_logp    [rows] fp32, required.
+ *   out_lse     [rows] fp32, or NULL.
+ * S is accumulated per 2048-element wave slice (fp32 exponentials of the slice's elements
+ * relative to its maximum, binary64 sums) and combined in slice order after rescaling to
+ * the row maximum: the same bits for every call with the same vocabulary, independent of
+ * the batch. Rows with a non-OK status get NaN in both outputs; greedy rows (T == 0) get
+ * logp 0 and lse +inf. The workspace is the one sized for TS_OP_SAMPLE_ROWS.
+ */
+int ts_sample_rows_logp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                        const int32_t* top_k, const float* top_p, const float* temperature,
+                        const uint64_t* seed, int32_t* out_token, float* out_logp, float* out_lse,
+                        int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic: the noise the sampler uses. For each tokens[j] of row `row` under `seed`,
  * writes the Philox word, u and g (all device arrays of n entries; any output may be NULL).
  */

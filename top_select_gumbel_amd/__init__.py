@@ -34,7 +34,7 @@ TS_KNOB_FORCE_EXACT = 2
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topp_mask",
-    "ts_sample_rows", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_logp", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -69,6 +69,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_topp_mask.restype = c.c_int
         lib.ts_sample_rows.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_sample_rows.restype = c.c_int
+        lib.ts_sample_rows_logp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ts_sample_rows_logp.restype = c.c_int
         lib.ts_gumbel_noise.argtypes = [c.c_uint64, i32, vp, i64, vp, vp, vp, vp]
         lib.ts_gumbel_noise.restype = c.c_int
         lib.ts_debug_set.argtypes = [c.c_int, i64]
@@ -185,6 +187,29 @@ def ts_sample_rows(logits, top_k, top_p, temperature, seed, out_token=None, stat
                               _ptr(temperature), _ptr(seed), _ptr(tok), _ptr(st), _ptr(ws),
                               ws.numel(), _stream()))
     return tok, st
+
+
+def ts_sample_rows_logp(logits, top_k, top_p, temperature, seed, want_lse: bool = True):
+    """Sample one token per row with its logprob: returns (tokens int32, logp fp32,
+    lse fp32 or None, status int32), each [rows]."""
+    import torch
+    lib = load_library()
+    rows, v, stride = _rows_view(logits)
+    top_k = _opt(top_k, "torch.int32", rows)
+    top_p = _opt(top_p, "torch.float32", rows)
+    temperature = _opt(temperature, "torch.float32", rows)
+    if seed is None or str(seed.dtype) not in ("torch.uint64", "torch.int64") or seed.numel() != rows:
+        raise TopSelectError("seed must be a uint64/int64 device tensor with one entry per row")
+    tok = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    logp = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(rows, dtype=torch.float32, device=logits.device) if want_lse else None
+    st = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    nb = lib.ts_workspace_bytes(TS_OP_SAMPLE_ROWS, rows, v, 0)
+    ws = workspace(nb, logits.device)
+    _check(lib.ts_sample_rows_logp(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
+                                   _ptr(temperature), _ptr(seed), _ptr(tok), _ptr(logp), _ptr(lse),
+                                   _ptr(st), _ptr(ws), ws.numel(), _stream()))
+    return tok, logp, lse, st
 
 
 def ts_gumbel_noise(seed: int, row: int, tokens):

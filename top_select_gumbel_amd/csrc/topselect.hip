@@ -126,6 +126,9 @@ struct Params {
   uint8_t* out_mask;
   int32_t* out_token;
   int32_t* status;
+  float* out_logp;             // sampling with logprobs: selected-token logprob, lse (or NULL)
+  float* out_lse;
+  double* wsum;                // per wave slice: sum of exp((x - wave max) / T), or NULL
   WaveInfo* info;
   uint2* cand;
 };
@@ -1038,6 +1041,29 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   const uint32_t kmax = wave_max(f2key(fmx));
   uint32_t flags = (__ballot(nan_any) != 0ull) ? kFlagNan : 0u;
   const int64_t seg = ((int64_t)r * P.chunks + c) * kW1 + w;
+  if (MODE == kModeSample && P.wsum) {
+    // [LOGP] "Design: the numeric contract": the wave's share of S = sum exp((x - m) / T),
+    // here relative to the wave maximum (the row kernel rescales each share to the row
+    // maximum). exp(y) = 2^(y log2 e) in fp32, four elements per fp32 partial, binary64
+    // accumulation, a fixed lane tree: the same bits for every launch of this vocabulary.
+    double acc = 0.0;
+    if (rp.bad == TS_ROW_OK && rp.t > 0.0f && kmax > kKeyNegInf && kmax < kKeyPosInf) {
+      const float m_w = key2f(kmax);
+      const float c2f = (float)(1.4426950408889634 / (double)rp.t);
+#pragma unroll
+      for (int s = 0; s < kS1; ++s) {
+        const int nv = nvalid(s);
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nv) ps += exp2f((xval(s, e) - m_w) * c2f);
+        acc += (double)ps;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (l == 0) P.wsum[seg] = acc;
+  }
 
   uint32_t count = 0, kmax_idx = 0xFFFFFFFFu;
   float best_s = -INFINITY;
@@ -1168,9 +1194,27 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
 }
 
 // ------------------------------------------------------------------ row kernel
+// Thread 0, sampling with logprobs: [LOGP] "Design: the numeric contract" with temperature in
+// the epilogue: logp = min(x_t / T - lse, 0) for the sampled token t. A rejected row
+// (tok < 0) gets NaN for both; greedy rows (T == 0) get lse = +inf and logp = 0.
+__device__ __forceinline__ void put_logp(const Params& P, int r, int32_t tok, float t, double lse) {
+  if (!P.out_logp && !P.out_lse) return;
+  float lp = __builtin_nanf(""), ls = __builtin_nanf("");
+  if (tok >= 0 && t == 0.0f) {
+    lp = 0.0f;
+    ls = INFINITY;
+  } else if (tok >= 0) {
+    const double xt = (double)P.x[(int64_t)r * P.stride + tok];
+    lp = (float)fmin(xt / (double)t - lse, 0.0);
+    ls = (float)lse;
+  }
+  if (P.out_logp) P.out_logp[r] = lp;
+  if (P.out_lse) P.out_lse[r] = ls;
+}
+
 template <int MODE>
 __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, int r, uint32_t kmax, uint32_t klo,
-                                            uint64_t seed, uint32_t total, const Sel& sk, Smem& sm) {
+                                            uint64_t seed, uint32_t total, const Sel& sk, Smem& sm, double lse) {
   // K = the candidates selected by sk, compacted into (kkey, kidx) in any order: every step
   // below is order-independent.
   const uint32_t nk = min(append_members(sm.ckey, sm.cidx, total,
@@ -1254,13 +1298,16 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
       }
     }
     const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
-    if (threadIdx.x == 0) P.out_token[r] = tok;
+    if (threadIdx.x == 0) {
+      P.out_token[r] = tok;
+      put_logp(P, r, tok, t, lse);
+    }
   }
 }
 
 template <int MODE>
 __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
-                                           uint32_t kmin, uint64_t seed, Smem& sm) {
+                                           uint32_t kmin, uint64_t seed, Smem& sm, double lse) {
   // The exact path over the raw row in global memory, one read of the row per pass.
   const float* row = P.x + (int64_t)r * P.stride;
   const uint32_t V = (uint32_t)P.V;
@@ -1433,7 +1480,10 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       bar();
     }
     const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
-    if (threadIdx.x == 0) P.out_token[r] = tok;
+    if (threadIdx.x == 0) {
+      P.out_token[r] = tok;
+      put_logp(P, r, tok, t, lse);
+    }
   }
 }
 
@@ -1607,6 +1657,21 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   }
   if (st == TS_ROW_OK) st = rp.bad;
   if (threadIdx.x == 0 && P.status) P.status[r] = st;
+  // Sampling with logprobs: lse = m/T + log S over the whole row, S combined from the wave
+  // shares in wave order, each rescaled from its wave maximum to the row maximum m.
+  double lse = 0.0;
+  if (MODE == kModeSample && P.wsum) {
+    double zpart = 0.0;
+    if (st == TS_ROW_OK && rp.t > 0.0f) {
+      const double m = (double)key2f(kmax);
+      for (int i = threadIdx.x; i < nseg; i += kRT) {
+        const uint32_t kw = inf[i].kmax;
+        if (kw > kKeyNegInf) zpart += P.wsum[(int64_t)r * nseg + i] * exp(((double)key2f(kw) - m) / (double)rp.t);
+      }
+    }
+    const double z = block_sum_f64<kRW>(zpart, reinterpret_cast<double*>(sm.red64));
+    lse = (double)key2f(kmax) / (double)rp.t + log(z);
+  }
 
   if (st != TS_ROW_OK) {
     if (MODE == kModeTopp && rp.path == kPathFull && P.out_mask) {
@@ -1617,7 +1682,10 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     } else if (MODE == kModeTopp) {
       if (threadIdx.x == 0) P.out_kept[r] = 0;
     } else {
-      if (threadIdx.x == 0) P.out_token[r] = -1;
+      if (threadIdx.x == 0) {
+        P.out_token[r] = -1;
+        put_logp(P, r, -1, rp.t, lse);
+      }
     }
     return;
   }
@@ -1637,7 +1705,10 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
         if (P.out_mask && idx < (uint32_t)P.V) P.out_mask[(int64_t)r * P.V + idx] = 1;
       }
     } else if (MODE == kModeSample) {
-      if (threadIdx.x == 0) P.out_token[r] = (int32_t)idx;
+      if (threadIdx.x == 0) {
+        P.out_token[r] = (int32_t)idx;
+        put_logp(P, r, (int32_t)idx, rp.t, lse);
+      }
     }
     return;
   }
@@ -1654,7 +1725,10 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
         if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
       }
       bi = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
-      if (threadIdx.x == 0) P.out_token[r] = bi;
+      if (threadIdx.x == 0) {
+        P.out_token[r] = bi;
+        put_logp(P, r, bi, rp.t, lse);
+      }
     }
     return;
   }
@@ -1771,12 +1845,12 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
           return;
         }
-        finish_cand<MODE>(P, rp, r, kmax, max(lo_key, min_sel), seed, ntot, sk, sm);
+        finish_cand<MODE>(P, rp, r, kmax, max(lo_key, min_sel), seed, ntot, sk, sm, lse);
         return;
       }
     }
   }
-  row_stream<MODE>(P, rp, r, kmax, kfloor, seed, sm);
+  row_stream<MODE>(P, rp, r, kmax, kfloor, seed, sm, lse);
 }
 
 __global__ void ts_fill_kernel(uint32_t* p, size_t n_words) {
@@ -1843,13 +1917,14 @@ int check_device(int* dev_out) {
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
-  size_t off_info = 0, off_cand = 0, total = 0;
+  size_t off_info = 0, off_cand = 0, off_wsum = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Chunking of a row and the workspace layout: per (row, chunk, wave) a WaveInfo, then per
-// (row, chunk, wave) a slice of cap_w candidate slots.
+// (row, chunk, wave) a slice of cap_w candidate slots, then per (row, chunk, wave) one double
+// (the wave's exponential sum, used by sampling with logprobs).
 bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   if (rows < 0 || V < 1 || V > TS_MAX_VOCAB) return false;
   int64_t ce = g_knob_chunk.load();
@@ -1869,6 +1944,8 @@ bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   b += align256(nseg * sizeof(WaveInfo));
   pl.off_cand = b;
   b += align256(nseg * (size_t)pl.cap_w * sizeof(uint2));
+  pl.off_wsum = b;
+  b += align256(nseg * sizeof(double));
   pl.total = b;
   return true;
 }
@@ -1877,7 +1954,7 @@ template <int MODE>
 int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_t* k, int32_t k_max,
            const float* p, const float* t, const uint64_t* seed, int32_t* out_idx, int32_t* out_kept,
            uint8_t* out_mask, int32_t* out_token, int32_t* status, void* ws, size_t ws_bytes,
-           void* stream) {
+           void* stream, float* out_logp = nullptr, float* out_lse = nullptr) {
   if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (V < 1 || V > TS_MAX_VOCAB) return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)V);
@@ -1914,9 +1991,12 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.out_mask = out_mask;
   P.out_token = out_token;
   P.status = status;
+  P.out_logp = out_logp;
+  P.out_lse = out_lse;
   char* w = static_cast<char*>(ws);
   P.info = reinterpret_cast<WaveInfo*>(w + pl.off_info);
   P.cand = reinterpret_cast<uint2*>(w + pl.off_cand);
+  P.wsum = (out_logp || out_lse) ? reinterpret_cast<double*>(w + pl.off_wsum) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(ts_stream_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
   hipError_t e = hipGetLastError();
@@ -1985,6 +2065,17 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
   return launch<kModeSample>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, seed,
                              nullptr, nullptr, nullptr, out_token, row_status, workspace,
                              workspace_bytes, stream);
+}
+
+int ts_sample_rows_logp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                        const int32_t* top_k, const float* top_p, const float* temperature,
+                        const uint64_t* seed, int32_t* out_token, float* out_logp, float* out_lse,
+                        int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows > 0 && (!seed || !out_token || !out_logp))
+    return fail(TS_ERR_INVALID_ARG, "seed, out_token and out_logp are required");
+  return launch<kModeSample>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, seed,
+                             nullptr, nullptr, nullptr, out_token, row_status, workspace,
+                             workspace_bytes, stream, out_logp, out_lse);
 }
 
 int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n,

@@ -216,6 +216,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, u
 }
 // Argmax over the workgroup of (score, lowest id): every thread gets the winning id and
 // (through best_s) its score (reds, redi: NW entries each). A score of -inf loses to every
+// Workgroup sum of one double per thread in a fixed tree (lane butterfly, then the waves in
+// order): the same bits for every launch. red holds NW doubles. Every thread gets the sum.
+template <int NW>
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if (lane() == 0) red[wave()] = v;
+  bar();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[w];
+  bar();
+  return s;
+}
+
 // finite one; scores are never NaN.
 template <int NW>
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
