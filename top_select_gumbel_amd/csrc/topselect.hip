@@ -1624,7 +1624,11 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 template <int MODE>
 __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   __shared__ Smem sm;
-  const int r = (int)blockIdx.x;
+  // With the stream kernel's XCD mapping (rows 8x .. 8x + rows/8 - 1 on XCD x, workgroups
+  // being dealt round-robin over the 8 XCDs), workgroup b takes a row whose summaries and
+  // candidates were written on its own XCD.
+  const int b = (int)blockIdx.x;
+  const int r = P.xcd_map ? (b & 7) * (P.rows >> 3) + (b >> 3) : b;
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
   // Aggregate the wave summaries. Their loads are issued first; the row parameters and the
