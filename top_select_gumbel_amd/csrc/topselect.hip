@@ -1150,6 +1150,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
     const float m_w = key2f(kmax);
     const uint64_t sd = P.seed[r];
     const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
+    const float inv_t = 1.0f / rp.t;   // one rounding per row instead of a division per token
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
 #pragma unroll
@@ -1164,7 +1165,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
         for (int e = 0; e < 4; ++e) {
           if (e < nv) {
             const float g = gumbel_from_uniform(uniform_from_word(words[e]));
-            const float sc = (xval(s, e) - m_w) / rp.t + g;
+            const float sc = (xval(s, e) - m_w) * inv_t + g;
             const int32_t id = (int32_t)(tok0 + e);
             if (sc > bs || (sc == bs && id < bi)) { bs = sc; bi = id; }
           }
