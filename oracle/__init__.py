@@ -13,6 +13,7 @@ chi-square / z tests of the sampling law. No function here is "parity unpinned".
 from .philox import philox4x32, philox4x32_np, seed_key, token_words
 from .sampler import (
     STATUS_BAD_K,
+    STATUS_BAD_MINP,
     STATUS_BAD_P,
     STATUS_BAD_T,
     STATUS_NONFINITE,
@@ -24,15 +25,20 @@ from .sampler import (
     gumbel_from_word,
     gumbel_noise,
     lse_logp_row,
+    minp_filter,
     neumaier_first_reach,
     row_floats,
     sample_logp_rows,
+    sample_minp_row,
+    sample_rows_minp,
     sample_row,
     sample_rows,
     to_f32,
     topk_select,
     topk_select_row,
     topp_mask,
+    topp_minp_mask,
+    topp_minp_row,
     topp_row,
     uniform_from_word,
 )

@@ -46,6 +46,7 @@ STATUS_NONFINITE = 1
 STATUS_BAD_K = 2
 STATUS_BAD_P = 3
 STATUS_BAD_T = 4
+STATUS_BAD_MINP = 5
 
 U_MIN = 2.0 ** -32          # smallest nonzero value of word * 2^-32
 U_MAX = 1.0 - 2.0 ** -24    # largest fp32 below 1.0: keeps log1p(-u) finite
@@ -133,6 +134,7 @@ class ToppResult:
     z: float = 0.0
     target: float = 0.0
     ambiguous: bool = False             # oracle_boundary_ambiguous ([TOPP] step 6)
+    minp_ambiguous: bool = False        # a kept weight within 1e-6 of min_p
     m: float = 0.0                      # row maximum logit
     x: List[float] = field(default_factory=list)
 
@@ -295,6 +297,57 @@ def sample_logp_rows(x2d, k, p, t, seeds):
     return out
 
 
+MINP_AMBIGUOUS_REL = 1e-6
+
+
+def minp_filter(res: ToppResult, min_p: Optional[float]) -> ToppResult:
+    """min-p after top-p, the pinned transform order temperature -> top-k -> top-p -> min-p
+    ([LOGP] relay program with pinned order; [REJ] "Task": min-p on probabilities).
+
+    A token of P stays when its probability is at least min_p times the largest one:
+    w_i / Z >= min_p * (1 / Z), i.e. w_i >= min_p with the binary64 weights of the top-p
+    step (w = 1 for the row maximum, which therefore always stays). Weights fall along the
+    canonical order, so the result is again a canonical prefix. min_p = 0 (or None) is off;
+    min_p must lie in [0, 1] (else status 5, after the checks of the other parameters).
+    ``minp_ambiguous`` marks rows where a weight of P lies within 1e-6 (relative) of min_p,
+    where a result computed in another precision may legitimately differ.
+    """
+    if min_p is None or res.status != STATUS_OK:
+        return res
+    mp = float(min_p)
+    if not (mp >= 0.0 and mp <= 1.0):
+        return ToppResult(status=STATUS_BAD_MINP, x=res.x)
+    if mp == 0.0 or not res.weights:     # off, or greedy (only the maximum is kept)
+        return res
+    w = res.weights
+    n = 0
+    while n < res.kept and w[n] >= mp:
+        n += 1
+    out = ToppResult(status=STATUS_OK, order=res.order, topk=res.topk, weights=res.weights,
+                     z=res.z, target=res.target, ambiguous=res.ambiguous, m=res.m, x=res.x)
+    out.kept = n
+    out.kept_ids = res.kept_ids[:n]
+    out.minp_ambiguous = any(abs(w[i] - mp) <= MINP_AMBIGUOUS_REL * mp for i in range(res.kept))
+    return out
+
+
+def topp_minp_row(row, k, p, t, min_p) -> ToppResult:
+    """Top-k, top-p, then min-p over one row."""
+    return minp_filter(topp_row(row, k, p, t), min_p)
+
+
+def sample_minp_row(row, k, p, t, min_p, seed: int, row_index: int) -> SampleResult:
+    """One sampled token id for one row after top-k, top-p and min-p."""
+    tp = topp_minp_row(row, k, p, t, min_p)
+    if tp.status != STATUS_OK:
+        return SampleResult(status=tp.status, topp=tp)
+    tv = 1.0 if t is None else float(t)
+    if tv == 0.0:
+        return SampleResult(status=STATUS_OK, token=tp.order[0], gap=math.inf, topp=tp)
+    tok, gap = gumbel_argmax(tp.x, tp.m, tv, tp.kept_ids, seed, row_index)
+    return SampleResult(status=STATUS_OK, token=tok, gap=gap, topp=tp)
+
+
 # --------------------------------------------------------------------------- batched
 def _opt(arr, r, cast):
     return None if arr is None else cast(arr[r])
@@ -325,4 +378,20 @@ def sample_rows(x2d, k, p, t, seeds):
     x2d = np.asarray(x2d, dtype=np.float32)
     return [sample_row(x2d[r], _opt(k, r, int), _opt(p, r, to_f32), _opt(t, r, to_f32),
                        int(seeds[r]), r)
+            for r in range(x2d.shape[0])]
+
+
+def topp_minp_mask(x2d, k, p, t, min_p):
+    """Batched top-k / top-p / min-p: list of ToppResult, one per row."""
+    x2d = np.asarray(x2d, dtype=np.float32)
+    return [topp_minp_row(x2d[r], _opt(k, r, int), _opt(p, r, to_f32), _opt(t, r, to_f32),
+                          _opt(min_p, r, to_f32))
+            for r in range(x2d.shape[0])]
+
+
+def sample_rows_minp(x2d, k, p, t, min_p, seeds):
+    """Batched sampling after top-k / top-p / min-p (row index = Philox row word)."""
+    x2d = np.asarray(x2d, dtype=np.float32)
+    return [sample_minp_row(x2d[r], _opt(k, r, int), _opt(p, r, to_f32), _opt(t, r, to_f32),
+                            _opt(min_p, r, to_f32), int(seeds[r]), r)
             for r in range(x2d.shape[0])]
