@@ -42,7 +42,7 @@
  *   - Per-row problems are reported in row_status[r] (if row_status is non-NULL) and the
  *     row's outputs are poisoned (-1 ids, kept count 0, all-zero mask row); other rows are
  *     unaffected. Codes, by precedence: TS_ROW_NONFINITE, TS_ROW_BAD_K, TS_ROW_BAD_P,
- *     TS_ROW_BAD_T.
+ *     TS_ROW_BAD_T, TS_ROW_BAD_MINP.
  *   - Host-side argument errors return a negative TS_ERR_* code before anything is
  *     enqueued; ts_last_error() then holds a thread-local message.
  *   - Workspace: device memory of at least ts_workspace_bytes(op, rows, vocab, k_max)
@@ -75,6 +75,7 @@ extern "C" {
 #define TS_ROW_BAD_K        2      /* k < 1, or (ts_topk_select) min(k, row_len) > k_max */
 #define TS_ROW_BAD_P        3      /* p not in (0, 1] (NaN included) */
 #define TS_ROW_BAD_T        4      /* temperature negative, NaN or infinite */
+#define TS_ROW_BAD_MINP     5      /* min_p outside [0, 1] or NaN (the _minp entry points) */
 
 /* Operation ids for ts_workspace_bytes. */
 #define TS_OP_TOPK_SELECT   0
@@ -156,6 +157,29 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
 int ts_sample_rows_logp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
                         const int32_t* top_k, const float* top_p, const float* temperature,
                         const uint64_t* seed, int32_t* out_token, float* out_logp, float* out_lse,
+                        int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ts_topp_mask_minp, ts_sample_rows_minp -- ts_topp_mask and ts_sample_rows with a min-p
+ * step after top-p, in the pinned transform order temperature -> top-k -> top-p -> min-p
+ * ([LOGP] "Integration", relay program with pinned order; [REJ] "Task": min-p on
+ * probabilities). A token of the top-p set stays when its probability is at least
+ * min_p[r] times the row's largest, i.e. when exp((x - max) / T) >= min_p[r]; the row maximum
+ * always stays and the result is again a prefix of the row ordering (out_kept, out_mask and
+ * the sampled token refer to it).
+ *   min_p   [rows] fp32, required: 0 = off; outside [0, 1] or NaN -> TS_ROW_BAD_MINP.
+ * The weight is the one the top-p step uses (an fp32 exp2 of a binary64 exponent, about
+ * 1.6e-7 relative), so a token whose weight lies within that of min_p can fall on either
+ * side. Rows that would take the full-row path (top-k and top-p off) take the exact
+ * row-streaming path when min-p is on. Other arguments as for ts_topp_mask / ts_sample_rows.
+ */
+int ts_topp_mask_minp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                      const int32_t* top_k, const float* top_p, const float* temperature,
+                      const float* min_p, int32_t* out_kept, uint8_t* out_mask, int32_t* row_status,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int ts_sample_rows_minp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                        const int32_t* top_k, const float* top_p, const float* temperature,
+                        const float* min_p, const uint64_t* seed, int32_t* out_token,
                         int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -26,6 +26,7 @@ TS_ROW_NONFINITE = 1
 TS_ROW_BAD_K = 2
 TS_ROW_BAD_P = 3
 TS_ROW_BAD_T = 4
+TS_ROW_BAD_MINP = 5
 TS_OP_TOPK_SELECT = 0
 TS_OP_TOPP_MASK = 1
 TS_OP_SAMPLE_ROWS = 2
@@ -34,7 +35,7 @@ TS_KNOB_FORCE_EXACT = 2
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topp_mask",
-    "ts_sample_rows", "ts_sample_rows_logp", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -71,6 +72,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_sample_rows.restype = c.c_int
         lib.ts_sample_rows_logp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_sample_rows_logp.restype = c.c_int
+        lib.ts_topp_mask_minp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ts_topp_mask_minp.restype = c.c_int
+        lib.ts_sample_rows_minp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ts_sample_rows_minp.restype = c.c_int
         lib.ts_gumbel_noise.argtypes = [c.c_uint64, i32, vp, i64, vp, vp, vp, vp]
         lib.ts_gumbel_noise.restype = c.c_int
         lib.ts_debug_set.argtypes = [c.c_int, i64]
@@ -210,6 +215,51 @@ def ts_sample_rows_logp(logits, top_k, top_p, temperature, seed, want_lse: bool 
                                    _ptr(temperature), _ptr(seed), _ptr(tok), _ptr(logp), _ptr(lse),
                                    _ptr(st), _ptr(ws), ws.numel(), _stream()))
     return tok, logp, lse, st
+
+
+def ts_topp_mask_minp(logits, top_k, top_p, temperature, min_p, want_mask: bool = True):
+    """Top-k, top-p then min-p: returns (kept int32 [rows], mask uint8 [rows, vocab] or None, status)."""
+    import torch
+    lib = load_library()
+    rows, v, stride = _rows_view(logits)
+    top_k = _opt(top_k, "torch.int32", rows)
+    top_p = _opt(top_p, "torch.float32", rows)
+    temperature = _opt(temperature, "torch.float32", rows)
+    min_p = _opt(min_p, "torch.float32", rows)
+    if min_p is None:
+        raise TopSelectError("min_p is required")
+    kept = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    mask = torch.empty((rows, v), dtype=torch.uint8, device=logits.device) if want_mask else None
+    st = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    nb = lib.ts_workspace_bytes(TS_OP_TOPP_MASK, rows, v, 0)
+    ws = workspace(nb, logits.device)
+    _check(lib.ts_topp_mask_minp(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
+                                 _ptr(temperature), _ptr(min_p), _ptr(kept), _ptr(mask), _ptr(st),
+                                 _ptr(ws), ws.numel(), _stream()))
+    return kept, mask, st
+
+
+def ts_sample_rows_minp(logits, top_k, top_p, temperature, min_p, seed):
+    """Sample after top-k, top-p and min-p: returns (tokens int32 [rows], status int32 [rows])."""
+    import torch
+    lib = load_library()
+    rows, v, stride = _rows_view(logits)
+    top_k = _opt(top_k, "torch.int32", rows)
+    top_p = _opt(top_p, "torch.float32", rows)
+    temperature = _opt(temperature, "torch.float32", rows)
+    min_p = _opt(min_p, "torch.float32", rows)
+    if min_p is None:
+        raise TopSelectError("min_p is required")
+    if seed is None or str(seed.dtype) not in ("torch.uint64", "torch.int64") or seed.numel() != rows:
+        raise TopSelectError("seed must be a uint64/int64 device tensor with one entry per row")
+    tok = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    st = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    nb = lib.ts_workspace_bytes(TS_OP_SAMPLE_ROWS, rows, v, 0)
+    ws = workspace(nb, logits.device)
+    _check(lib.ts_sample_rows_minp(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
+                                   _ptr(temperature), _ptr(min_p), _ptr(seed), _ptr(tok), _ptr(st),
+                                   _ptr(ws), ws.numel(), _stream()))
+    return tok, st
 
 
 def ts_gumbel_noise(seed: int, row: int, tokens):

@@ -114,6 +114,7 @@ struct Params {
   const int32_t* k;
   const float* p;
   const float* t;
+  const float* minp;           // min-p per row, or NULL (off)
   const uint64_t* seed;
   int32_t k_max;
   int32_t chunks;
@@ -137,6 +138,7 @@ struct RowPlan {
   int32_t k_eff;
   float p;
   float t;
+  float minp;                  // 0 = off
   int32_t path;
   int32_t bad;
 };
@@ -180,17 +182,19 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int mode, int r) {
   rp.k_eff = kr < 1 ? 0 : min(kr, P.V);
   rp.p = (mode != kModeTopk && P.p) ? P.p[r] : 1.0f;
   rp.t = (mode != kModeTopk && P.t) ? P.t[r] : 1.0f;
+  rp.minp = (mode != kModeTopk && P.minp) ? P.minp[r] : 0.0f;
   int bad = TS_ROW_OK;
   if (kr < 1) bad = TS_ROW_BAD_K;
   else if (mode == kModeTopk && rp.k_eff > P.k_max) bad = TS_ROW_BAD_K;
   else if (mode != kModeTopk && !(rp.p > 0.0f && rp.p <= 1.0f)) bad = TS_ROW_BAD_P;
   else if (mode != kModeTopk && !(rp.t >= 0.0f && rp.t <= FLT_MAX)) bad = TS_ROW_BAD_T;
+  else if (mode != kModeTopk && !(rp.minp >= 0.0f && rp.minp <= 1.0f)) bad = TS_ROW_BAD_MINP;
   rp.bad = bad;
   if (bad) rp.path = kPathNone;
   else if (mode == kModeTopk) rp.path = rp.k_eff <= kFastK ? kPathCand : kPathStream;
   else if (rp.t == 0.0f) rp.path = kPathGreedy;
   else if (rp.k_eff <= kFastK) rp.path = kPathCand;
-  else if (rp.k_eff == P.V && rp.p == 1.0f) rp.path = kPathFull;
+  else if (rp.k_eff == P.V && rp.p == 1.0f && rp.minp == 0.0f) rp.path = kPathFull;
   else rp.path = kPathStream;
   return rp;
 }
@@ -1271,22 +1275,34 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
     const uint64_t target_fx = topp_target(rp.p, zh);
     sp = select_mass(kvis, wmass, target_fx, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
   }
+  // min-p after top-p: the members of P whose weight is >= min_p (the maximum has weight 1),
+  // again a canonical prefix ([LOGP] relay order temperature -> top-k -> top-p -> min-p).
+  const double c2m = kLog2e / (double)t;
+  auto keep = [&](uint32_t rk, uint32_t idx) {
+    return sel_member(sp, rk, idx) && (rp.minp <= 0.0f || weight32(rk, m, c2m) >= rp.minp);
+  };
   if (MODE == kModeTopp) {
+    if (rp.minp > 0.0f) {
+      uint64_t c = 0, z = 0;
+      kvis([&](uint32_t rk, uint32_t idx) { c += keep(rk, idx) ? 1u : 0u; });
+      block_sum2_u64<kRW>(c, z, sm.red64);
+      kept = (uint32_t)c;
+    }
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
     if (P.out_mask) {
       uint8_t* mrow = P.out_mask + (int64_t)r * P.V;
       kvis([&](uint32_t rk, uint32_t idx) {
-        if (sel_member(sp, rk, idx) && idx < (uint32_t)P.V) mrow[idx] = 1;
+        if (keep(rk, idx) && idx < (uint32_t)P.V) mrow[idx] = 1;
       });
     }
   } else {
-    // Gumbel-max over the kept set P: the scores drawn above, masked by membership of P;
-    // without top-p P = K and the scores are drawn here.
+    // Gumbel-max over the kept set: the scores drawn above, masked by membership; without
+    // top-p P = K and the scores are drawn here.
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
     if (rp.p != 1.0f) {
       kvis_i(nk, [&](uint32_t i, uint32_t rk, uint32_t idx) {
-        if (sel_member(sp, rk, idx)) {
+        if (keep(rk, idx)) {
           const float sc = gsc[i];
           if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
         }
@@ -1294,6 +1310,7 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
     } else {
       for (uint32_t i = threadIdx.x; i < nk; i += kRT) {
         const uint32_t idx = sm.kidx[i];
+        if (!keep(sm.kkey[i], idx)) continue;
         const float sc = gumbel_score(sm.kkey[i], idx, m, t, (uint32_t)r, k0, k1);
         if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
       }
@@ -1404,12 +1421,23 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
     block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics
     sp = select_mass<true>(kvis, wmass, topp_target(rp.p, zh), ke, kmax, klo, 0u, V - 1, sm, kept, pre);
   }
+  // min-p after top-p (as on the candidate path)
+  const double c2m = kLog2e / (double)t;
+  auto keep = [&](uint32_t rk, uint32_t idx) {
+    return sel_member(sp, rk, idx) && (rp.minp <= 0.0f || weight32(rk, m, c2m) >= rp.minp);
+  };
   if (MODE == kModeTopp) {
+    if (rp.minp > 0.0f) {
+      uint64_t c = 0, z = 0;
+      kvis([&](uint32_t rk, uint32_t idx) { c += keep(rk, idx) ? 1u : 0u; });
+      block_sum2_u64<kRW>(c, z, sm.red64);
+      kept = (uint32_t)c;
+    }
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)kept;
     if (P.out_mask) {
       uint8_t* mrow = P.out_mask + (int64_t)r * P.V;
       kvis([&](uint32_t rk, uint32_t idx) {
-        if (sel_member(sp, rk, idx)) mrow[idx] = 1;
+        if (keep(rk, idx)) mrow[idx] = 1;
       });
     }
   } else {
@@ -1437,7 +1465,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       for (int u = 0; u < kPer; ++u) {
         const uint32_t i = s0 + (uint32_t)(u * kRT) + threadIdx.x;
         cur[u] = f2key(__uint_as_float(cur[u]));
-        bal[u] = __ballot(i < V && sel_member(sk, cur[u], i) && sel_member(sp, cur[u], i));
+        bal[u] = __ballot(i < V && sel_member(sk, cur[u], i) && keep(cur[u], i));
         tot += (uint32_t)__popcll(bal[u]);
       }
       if (tot) {   // wave-uniform: one reservation per wave and slab
@@ -1959,7 +1987,8 @@ template <int MODE>
 int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_t* k, int32_t k_max,
            const float* p, const float* t, const uint64_t* seed, int32_t* out_idx, int32_t* out_kept,
            uint8_t* out_mask, int32_t* out_token, int32_t* status, void* ws, size_t ws_bytes,
-           void* stream, float* out_logp = nullptr, float* out_lse = nullptr) {
+           void* stream, float* out_logp = nullptr, float* out_lse = nullptr,
+           const float* minp = nullptr) {
   if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (V < 1 || V > TS_MAX_VOCAB) return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)V);
@@ -1985,6 +2014,7 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.p = p;
   P.t = t;
   P.seed = seed;
+  P.minp = minp;
   P.k_max = k_max;
   P.chunks = (int32_t)pl.chunks;
   P.chunk_len = (int32_t)pl.chunk_len;
@@ -2083,6 +2113,27 @@ int ts_sample_rows_logp(const float* logits, int64_t rows, int64_t vocab, int64_
                              workspace_bytes, stream, out_logp, out_lse);
 }
 
+int ts_topp_mask_minp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                      const int32_t* top_k, const float* top_p, const float* temperature,
+                      const float* min_p, int32_t* out_kept, uint8_t* out_mask, int32_t* row_status,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows > 0 && (!out_kept || !min_p)) return fail(TS_ERR_INVALID_ARG, "min_p and out_kept are required");
+  return launch<kModeTopp>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, nullptr,
+                           nullptr, out_kept, out_mask, nullptr, row_status, workspace,
+                           workspace_bytes, stream, nullptr, nullptr, min_p);
+}
+
+int ts_sample_rows_minp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                        const int32_t* top_k, const float* top_p, const float* temperature,
+                        const float* min_p, const uint64_t* seed, int32_t* out_token,
+                        int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows > 0 && (!seed || !out_token || !min_p))
+    return fail(TS_ERR_INVALID_ARG, "min_p, seed and out_token are required");
+  return launch<kModeSample>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, seed,
+                             nullptr, nullptr, nullptr, out_token, row_status, workspace,
+                             workspace_bytes, stream, nullptr, nullptr, min_p);
+}
+
 int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n,
                     uint32_t* out_word, float* out_u, float* out_g, void* stream) {
   if (n < 0) return fail(TS_ERR_INVALID_ARG, "n < 0");
@@ -2121,6 +2172,7 @@ const char* ts_status_string(int status) {
     case TS_ROW_BAD_K: return "row k invalid";
     case TS_ROW_BAD_P: return "row top_p outside (0, 1]";
     case TS_ROW_BAD_T: return "row temperature negative or non-finite";
+    case TS_ROW_BAD_MINP: return "row min_p outside [0, 1]";
     default: return "unknown status";
   }
 }
