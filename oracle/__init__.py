@@ -34,8 +34,12 @@ from .sampler import (
     sample_row,
     sample_rows,
     to_f32,
+    ORDER_INDEX,
+    ORDER_VALUE,
     topk_select,
     topk_select_row,
+    topk_select_rows,
+    topk_select_rows_row,
     topp_mask,
     topp_minp_mask,
     topp_minp_row,

@@ -122,6 +122,53 @@ def topk_select_row(row, k: int, k_max: int):
     return STATUS_OK, chosen + [-1] * (k_max - ke)
 
 
+ORDER_INDEX = 0
+ORDER_VALUE = 1
+
+
+def topk_select_rows_row(row, length: Optional[int], k: int, k_max: int, order: int = ORDER_INDEX,
+                         offset: int = 0):
+    """Top-k of a row's valid prefix, for sparse-indexer rows of varying length.
+
+    [DETK] "Changes" (filtered-row length clamping) and "Test plan" (short rows padded with
+    -1): only keys [0, n) take part, n = length clamped to [0, len(row)] (None = the whole
+    row); a NaN there rejects the row (one past n does not). The selection is the first
+    min(k, n) ids of the canonical order of that prefix. Output order: ascending id
+    (ORDER_INDEX, as [DETK] emits) or the canonical order itself (ORDER_VALUE: value
+    descending, id ascending, as a value-ordered top-k returns it). Each emitted id is
+    shifted by ``offset`` (the row's start in a ragged index space); unused slots are -1.
+    """
+    x = row_floats(row)
+    n = len(x) if length is None else max(0, min(int(length), len(x)))
+    x = x[:n]
+    st = logits_status(x, select_only=True) if n > 0 else STATUS_OK
+    if st == STATUS_OK and int(k) < 1:
+        st = STATUS_BAD_K
+    ke = min(int(k), n) if st == STATUS_OK else 0
+    if st == STATUS_OK and ke > k_max:
+        st = STATUS_BAD_K
+    if st != STATUS_OK:
+        return st, [-1] * k_max
+    chosen = canonical_order(x)[:ke]
+    if order == ORDER_INDEX:
+        chosen = sorted(chosen)
+    return STATUS_OK, [offset + i for i in chosen] + [-1] * (k_max - ke)
+
+
+def topk_select_rows(x2d, lengths, k, k_max: int, order: int = ORDER_INDEX, offsets=None):
+    """Batched form of topk_select_rows_row: (status[B], out_idx[B, k_max]) int32 arrays."""
+    x2d = np.asarray(x2d, dtype=np.float32)
+    b = x2d.shape[0]
+    status = np.zeros(b, np.int32)
+    out = np.full((b, k_max), -1, np.int64)
+    for r in range(b):
+        st, idx = topk_select_rows_row(x2d[r], None if lengths is None else int(lengths[r]), int(k[r]), k_max,
+                                       order, 0 if offsets is None else int(offsets[r]))
+        status[r] = st
+        out[r] = idx
+    return status, out.astype(np.int32)
+
+
 # --------------------------------------------------------------------------- top-p
 @dataclass
 class ToppResult:
