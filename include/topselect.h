@@ -110,6 +110,28 @@ int ts_topk_select(const float* keys, int64_t rows, int64_t row_len, int64_t row
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ts_topk_select_rows -- ts_topk_select for sparse-indexer rows of varying length ([DETK]
+ * "Changes": filtered-row length clamping; "Test plan": short rows, -1 padding):
+ *   lengths  [rows] int32 or NULL: only keys [0, n) of row r take part, n = lengths[r]
+ *            clamped to [0, row_len]; NULL = row_len. A NaN at or past n is ignored. The
+ *            row's k_eff = min(k[r], n) (status TS_ROW_BAD_K if it exceeds k_max); an empty
+ *            row gives k_max slots of -1.
+ *   order    TS_ORDER_INDEX: the selected ids ascending (as ts_topk_select);
+ *            TS_ORDER_VALUE: in the row ordering itself, value descending then id ascending
+ *            (the order a value-ordered top-k returns); needs k_max <= 8192.
+ *   offsets  [rows] int32 or NULL: added to every emitted id of row r (the row's start in a
+ *            ragged index space); the caller keeps offset + id within int32.
+ * Other arguments and the workspace as for ts_topk_select (the workspace is sized with
+ * TS_OP_TOPK_SELECT for row_len).
+ */
+#define TS_ORDER_INDEX 0
+#define TS_ORDER_VALUE 1
+int ts_topk_select_rows(const float* keys, int64_t rows, int64_t row_len, int64_t row_stride,
+                        const int32_t* lengths, const int32_t* k, int32_t k_max, int order,
+                        const int32_t* offsets, int32_t* out_idx, int32_t* row_status, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * ts_topp_mask -- [TOPP] "Source basis" and "Independent binary64 numerical reference":
  * temperature -> top-k -> top-p. With w_i = exp((x_i - max)/T) over the top-k set K and
  * Z = sum_K w, the kept set P is the shortest prefix of K (in the row ordering) whose

@@ -27,6 +27,8 @@ TS_ROW_BAD_K = 2
 TS_ROW_BAD_P = 3
 TS_ROW_BAD_T = 4
 TS_ROW_BAD_MINP = 5
+TS_ORDER_INDEX = 0
+TS_ORDER_VALUE = 1
 TS_OP_TOPK_SELECT = 0
 TS_OP_TOPP_MASK = 1
 TS_OP_SAMPLE_ROWS = 2
@@ -34,7 +36,7 @@ TS_KNOB_CHUNK_ELEMS = 1
 TS_KNOB_FORCE_EXACT = 2
 
 EXPORTED = (
-    "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topp_mask",
+    "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",
     "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
@@ -66,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_workspace_init.restype = c.c_int
         lib.ts_topk_select.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
         lib.ts_topk_select.restype = c.c_int
+        lib.ts_topk_select_rows.argtypes = [vp, i64, i64, i64, vp, vp, i32, c.c_int, vp, vp, vp, vp, sz, vp]
+        lib.ts_topk_select_rows.restype = c.c_int
         lib.ts_topp_mask.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_topp_mask.restype = c.c_int
         lib.ts_sample_rows.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -152,6 +156,26 @@ def ts_topk_select(keys, k, k_max: int, row_len: Optional[int] = None):
     ws = workspace(nb, keys.device)
     _check(lib.ts_topk_select(_ptr(keys), rows, v, stride, _ptr(k), k_max, _ptr(out), _ptr(st),
                               _ptr(ws), ws.numel(), _stream()))
+    return out, st
+
+
+def ts_topk_select_rows(keys, k, k_max: int, lengths=None, order: int = 0, offsets=None,
+                        row_len: Optional[int] = None):
+    """Top-k over each row's valid prefix (lengths), ids ascending (order 0) or value-ordered
+    (order 1), shifted by offsets: returns (out_idx int32 [rows, k_max], status int32)."""
+    import torch
+    lib = load_library()
+    rows, cols, stride = _rows_view(keys)
+    v = cols if row_len is None else int(row_len)
+    k = _opt(k, "torch.int32", rows)
+    lengths = _opt(lengths, "torch.int32", rows)
+    offsets = _opt(offsets, "torch.int32", rows)
+    out = torch.empty((rows, k_max), dtype=torch.int32, device=keys.device)
+    st = torch.empty(rows, dtype=torch.int32, device=keys.device)
+    nb = lib.ts_workspace_bytes(TS_OP_TOPK_SELECT, rows, v, k_max)
+    ws = workspace(nb, keys.device)
+    _check(lib.ts_topk_select_rows(_ptr(keys), rows, v, stride, _ptr(lengths), _ptr(k), k_max, int(order),
+                                   _ptr(offsets), _ptr(out), _ptr(st), _ptr(ws), ws.numel(), _stream()))
     return out, st
 
 

@@ -115,6 +115,9 @@ struct Params {
   const float* p;
   const float* t;
   const float* minp;           // min-p per row, or NULL (off)
+  const int32_t* lengths;      // top-k select: valid keys per row (clamped to V), or NULL
+  const int32_t* offsets;      // top-k select: added to every emitted id, or NULL
+  int32_t order;               // top-k select: TS_ORDER_INDEX or TS_ORDER_VALUE
   const uint64_t* seed;
   int32_t k_max;
   int32_t chunks;
@@ -135,6 +138,7 @@ struct Params {
 };
 
 struct RowPlan {
+  int32_t n;                   // the row's valid length (V unless top-k select lengths are given)
   int32_t k_eff;
   float p;
   float t;
@@ -178,8 +182,9 @@ struct Smem1 {
 // ------------------------------------------------------------------ per-row plan
 __device__ __forceinline__ RowPlan plan_row(const Params& P, int mode, int r) {
   RowPlan rp;
+  rp.n = (mode == kModeTopk && P.lengths) ? max(0, min(P.lengths[r], P.V)) : P.V;
   const int32_t kr = P.k ? P.k[r] : P.V;
-  rp.k_eff = kr < 1 ? 0 : min(kr, P.V);
+  rp.k_eff = kr < 1 ? 0 : min(kr, rp.n);
   rp.p = (mode != kModeTopk && P.p) ? P.p[r] : 1.0f;
   rp.t = (mode != kModeTopk && P.t) ? P.t[r] : 1.0f;
   rp.minp = (mode != kModeTopk && P.minp) ? P.minp[r] : 0.0f;
@@ -895,7 +900,9 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
   const int r = L / P.chunks;
   const int c = L - r * P.chunks;
   const int c0 = c * P.chunk_len;
-  const int n = min(P.chunk_len, P.V - c0);
+  // the row's valid length: V, or its clamped length for top-k select rows of varying length
+  const int vrow = (MODE == kModeTopk && P.lengths) ? max(0, min(P.lengths[r], P.V)) : P.V;
+  const int n = max(0, min(P.chunk_len, vrow - c0));   // 0: the chunk lies past the row's end
   const float* base = P.x + (int64_t)r * P.stride + c0;
   const bool aligned = ((uintptr_t)base & 15u) == 0;
   const int nq = (n + 3) >> 2;
@@ -931,7 +938,7 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
         }
       }
     }
-  } else {
+  } else if (n > 0) {
     const uint32_t* s32 = reinterpret_cast<const uint32_t*>(base);
 #pragma unroll
     for (int s = 0; s < kS1; ++s) {
@@ -941,6 +948,9 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
       raw[s].z = s32[min(e0 + 2, n - 1)];
       raw[s].w = s32[min(e0 + 3, n - 1)];
     }
+  } else {   // empty chunk: nothing is loaded; -inf cannot raise a maximum or set a flag
+#pragma unroll
+    for (int s = 0; s < kS1; ++s) raw[s] = make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
   }
   // The row's parameters are read only now, so the chunk's loads above are already in
   // flight while these small loads resolve.
@@ -1199,6 +1209,36 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
 }
 
 // ------------------------------------------------------------------ row kernel
+// Top-k select output in the canonical order (value descending, id ascending): the cnt
+// selected items sit unordered in a[0, cnt) as (key << 32 | ~id); a bitonic network sorts
+// them descending in LDS (padding 0 sorts last: every real key is above 0), then row slot j
+// gets off + id_j. cnt <= cap, cap a power of two.
+__device__ __forceinline__ void emit_value_order(uint64_t* a, uint32_t cnt, uint32_t cap, int32_t* orow,
+                                                 uint32_t kmx, int32_t off) {
+  uint32_t nn = 1;
+  while (nn < cnt) nn <<= 1;
+  for (uint32_t i = cnt + threadIdx.x; i < nn; i += kRT) a[i] = 0ull;
+  bar();
+  for (uint32_t kk = 2; kk <= nn; kk <<= 1) {
+    for (uint32_t jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (uint32_t i = threadIdx.x; i < nn; i += kRT) {
+        const uint32_t l = i ^ jj;
+        if (l > i) {
+          const uint64_t x = a[i], y = a[l];
+          const bool desc = (i & kk) == 0;   // this pair's block sorts descending
+          if (desc ? x < y : x > y) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      bar();
+    }
+  }
+  (void)cap;
+  for (uint32_t j = threadIdx.x; j < cnt && j < kmx; j += kRT) orow[j] = off + (int32_t)(~(uint32_t)a[j]);
+}
+
 // Thread 0, sampling with logprobs: [LOGP] "Design: the numeric contract" with temperature in
 // the epilogue: logp = min(x_t / T - lse, 0) for the sampled token t. A rejected row
 // (tok < 0) gets NaN for both; greedy rows (T == 0) get lse = +inf and logp = 0.
@@ -1328,7 +1368,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
                                            uint32_t kmin, uint64_t seed, Smem& sm, double lse) {
   // The exact path over the raw row in global memory, one read of the row per pass.
   const float* row = P.x + (int64_t)r * P.stride;
-  const uint32_t V = (uint32_t)P.V;
+  const uint32_t V = (uint32_t)rp.n;   // the row's valid length
   const bool al4 = ((uintptr_t)row & 15u) == 0;
   auto rvis = [&](auto f) {
     if (al4) {   // 8 float4 loads per thread per round; the next round loads during this one
@@ -1383,10 +1423,28 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   if (MODE == kModeTopk) {
     int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
     const uint32_t kmx = (uint32_t)P.k_max;
-    uint32_t run = 0;
-    emit_ordered<4>(V, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = f2key(row[i]); idx = i; },
-                    [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                    [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
+    const int32_t off = P.offsets ? P.offsets[r] : 0;
+    if (P.order == TS_ORDER_VALUE) {
+      // K (<= 8192 items, checked by the host) gathered from the row into the free candidate
+      // arrays, then sorted there
+      uint64_t* a = reinterpret_cast<uint64_t*>(sm.ckey);
+      rvis([&](uint32_t rk, uint32_t idx) {
+        if (sel_member(sk, rk, idx)) {
+          const uint32_t at = atomicAdd(&sm.bcount, 1u);
+          if (at < (uint32_t)(kLdsCand)) a[at] = ((uint64_t)rk << 32) | (uint32_t)~idx;
+        }
+      });
+      bar();
+      const uint32_t nk = min(sm.bcount, (uint32_t)kLdsCand);
+      bar();
+      if (threadIdx.x == 0) sm.bcount = 0;
+      emit_value_order(a, nk, (uint32_t)kLdsCand, orow, kmx, off);
+    } else {
+      uint32_t run = 0;
+      emit_ordered<4>(V, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = f2key(row[i]); idx = i; },
+                      [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                      [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = off + (int32_t)idx; }, run, sm);
+    }
     for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
     return;
   }
@@ -1790,7 +1848,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     // Wave w published the elements >= its threshold (at most the cap of them when it
     // overflowed): at least `total` elements are >= cmin, so the k-th key is >= cmin (used
     // only when a top-k select runs, k < V).
-    if (total >= ke && ke < (uint32_t)P.V) kfloor = cmin;
+    if (total >= ke && ke < (uint32_t)rp.n) kfloor = cmin;
     const bool fast = !P.force_exact && (flags & kFlagOverflow) == 0 && total >= ke;
     uint32_t ntot = 0, lo_key = cmin;
     bool pre = false;
@@ -1871,10 +1929,23 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
         if (MODE == kModeTopk) {
           int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
           const uint32_t kmx = (uint32_t)P.k_max;
-          uint32_t run = 0;
-          emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
-                          [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                          [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = (int32_t)idx; }, run, sm);
+          const int32_t off = P.offsets ? P.offsets[r] : 0;
+          if (P.order == TS_ORDER_VALUE) {
+            // K (<= kFastK items) compacted, then sorted in the free mass histogram
+            const uint32_t nk = min(append_members(sm.ckey, sm.cidx, ntot,
+                                                   [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                                                   sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
+                                    (uint32_t)kFastK);
+            uint64_t* a = reinterpret_cast<uint64_t*>(sm.mhi);
+            for (uint32_t i = threadIdx.x; i < nk; i += kRT) a[i] = ((uint64_t)sm.kkey[i] << 32) | (uint32_t)~sm.kidx[i];
+            emit_value_order(a, nk, (uint32_t)kDBins, orow, kmx, off);
+          } else {
+            uint32_t run = 0;
+            emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
+                            [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                            [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = off + (int32_t)idx; },
+                            run, sm);
+          }
           for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
           return;
         }
@@ -1988,7 +2059,8 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
            const float* p, const float* t, const uint64_t* seed, int32_t* out_idx, int32_t* out_kept,
            uint8_t* out_mask, int32_t* out_token, int32_t* status, void* ws, size_t ws_bytes,
            void* stream, float* out_logp = nullptr, float* out_lse = nullptr,
-           const float* minp = nullptr) {
+           const float* minp = nullptr, const int32_t* lengths = nullptr, const int32_t* offsets = nullptr,
+           int order = TS_ORDER_INDEX) {
   if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (V < 1 || V > TS_MAX_VOCAB) return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)V);
@@ -2015,6 +2087,9 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.t = t;
   P.seed = seed;
   P.minp = minp;
+  P.lengths = lengths;
+  P.offsets = offsets;
+  P.order = order;
   P.k_max = k_max;
   P.chunks = (int32_t)pl.chunks;
   P.chunk_len = (int32_t)pl.chunk_len;
@@ -2072,14 +2147,26 @@ int ts_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   return TS_OK;
 }
 
+int ts_topk_select_rows(const float* keys, int64_t rows, int64_t row_len, int64_t row_stride,
+                        const int32_t* lengths, const int32_t* k, int32_t k_max, int order,
+                        const int32_t* offsets, int32_t* out_idx, int32_t* row_status, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (rows > 0 && (!k || !out_idx)) return fail(TS_ERR_INVALID_ARG, "k and out_idx are required");
+  if (k_max < 1) return fail(TS_ERR_INVALID_ARG, "k_max = %d < 1", (int)k_max);
+  if (order != TS_ORDER_INDEX && order != TS_ORDER_VALUE)
+    return fail(TS_ERR_INVALID_ARG, "order = %d is neither TS_ORDER_INDEX nor TS_ORDER_VALUE", order);
+  if (order == TS_ORDER_VALUE && k_max > kLdsCand)
+    return fail(TS_ERR_INVALID_ARG, "value order supports k_max <= %d (got %d)", kLdsCand, (int)k_max);
+  return launch<kModeTopk>(keys, rows, row_len, row_stride, k, k_max, nullptr, nullptr, nullptr,
+                           out_idx, nullptr, nullptr, nullptr, row_status, workspace,
+                           workspace_bytes, stream, nullptr, nullptr, nullptr, lengths, offsets, order);
+}
+
 int ts_topk_select(const float* keys, int64_t rows, int64_t row_len, int64_t row_stride,
                    const int32_t* k, int32_t k_max, int32_t* out_idx, int32_t* row_status,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (rows > 0 && (!k || !out_idx)) return fail(TS_ERR_INVALID_ARG, "k and out_idx are required");
-  if (k_max < 1) return fail(TS_ERR_INVALID_ARG, "k_max = %d < 1", (int)k_max);
-  return launch<kModeTopk>(keys, rows, row_len, row_stride, k, k_max, nullptr, nullptr, nullptr,
-                           out_idx, nullptr, nullptr, nullptr, row_status, workspace,
-                           workspace_bytes, stream);
+  return ts_topk_select_rows(keys, rows, row_len, row_stride, nullptr, k, k_max, TS_ORDER_INDEX, nullptr,
+                             out_idx, row_status, workspace, workspace_bytes, stream);
 }
 
 int ts_topp_mask(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
