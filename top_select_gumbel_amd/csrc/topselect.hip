@@ -74,6 +74,7 @@ constexpr int kH2Bits = 8;                          // second-level digit inside
 constexpr int kH2Bins = 1 << kH2Bits;
 constexpr int kSampleSlots = 2;                     // slots whose keys form the sample
 constexpr int kQStage = 128;                        // staged quads per wave
+constexpr int kRefine = 16;                         // sampled keys in a chosen bin that call for a finer level
 constexpr int kCapW = kChunkMax / kW1;              // candidate slots per wave: its whole share, so a
                                                      // slice cannot overflow (massive ties stay exact)
 // row kernel
@@ -855,7 +856,8 @@ __device__ __forceinline__ void search_hist(const uint32_t* hist, uint32_t thr, 
   }
 }
 
-// Wave 0 only: the same search over the 256-bin second level (four bins per lane).
+// Wave 0 only: the same search over the 256-bin second level (four bins per lane); also
+// writes res[1] = count in bins above b and res[2] = count in b.
 __device__ __forceinline__ void search_hist2(const uint32_t* hist, uint32_t thr, Smem1& sm) {
   const int l = lane();
   const uint4 v = reinterpret_cast<const uint4*>(hist)[l];
@@ -872,6 +874,8 @@ __device__ __forceinline__ void search_hist2(const uint32_t* hist, uint32_t thr,
       acc += c[j];
     }
     sm.res[0] = (uint32_t)(4 * L + j);
+    sm.res[1] = acc;
+    sm.res[2] = c[j];
   }
 }
 
@@ -889,7 +893,7 @@ __device__ __forceinline__ void fill_bytes_nt(uint8_t* dst, int64_t n, uint8_t v
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
+__global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void ts_stream_kernel(Params P) {
   __shared__ Smem1 sm;
   const int b = (int)blockIdx.x;
   int L = b;
@@ -1018,7 +1022,34 @@ __global__ __launch_bounds__(kT1) void ts_stream_kernel(Params P) {
       bar();
       if (w == 0) search_hist2(sm.hist2, need2, sm);
       bar();
-      const uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - kHBits - kH2Bits));
+      uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - kHBits - kH2Bits));
+      uint32_t in_bin = sm.res[2], need = need2 - sm.res[1];
+      // Narrow value ranges (a near-uniform row puts every sampled key in one 2^13-key bin):
+      // refine through the remaining 13 key bits, 8 then 5 at a time, while the chosen bin
+      // still holds more than kRefine sampled keys. Never taken on spread-out rows.
+#pragma unroll 1
+      for (int lvl = 0; lvl < 2 && in_bin > (uint32_t)kRefine; ++lvl) {
+        const int sh = lvl == 0 ? 5 : 0;
+        const int bits = lvl == 0 ? 8 : 5;
+        const uint32_t pre = tk >> (sh + bits);
+        if (threadIdx.x < kH2Bins) sm.hist2[threadIdx.x] = 0u;
+        bar();
+#pragma unroll
+        for (int s = 0; s < kSampleSlots; ++s) {
+          const int nv = nvalid(s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = f2key(xval(s, e));
+            if (e < nv && (key >> (sh + bits)) == pre) atomicAdd(&sm.hist2[(key >> sh) & ((1u << bits) - 1u)], 1u);
+          }
+        }
+        bar();
+        if (w == 0) search_hist2(sm.hist2, need, sm);
+        bar();
+        tk |= sm.res[0] << sh;
+        in_bin = sm.res[2];
+        need -= sm.res[1];
+      }
       if (tk > kKeyNegInf) {
         thr = tk;
         thr_f = key2f(tk);
@@ -1318,8 +1349,11 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
   // min-p after top-p: the members of P whose weight is >= min_p (the maximum has weight 1),
   // again a canonical prefix ([LOGP] relay order temperature -> top-k -> top-p -> min-p).
   const double c2m = kLog2e / (double)t;
+  const bool minp_on = rp.minp > 0.0f;   // uniform: the weight is computed only when min-p is on
   auto keep = [&](uint32_t rk, uint32_t idx) {
-    return sel_member(sp, rk, idx) && (rp.minp <= 0.0f || weight32(rk, m, c2m) >= rp.minp);
+    bool in = sel_member(sp, rk, idx);
+    if (minp_on) in = in && weight32(rk, m, c2m) >= rp.minp;
+    return in;
   };
   if (MODE == kModeTopp) {
     if (rp.minp > 0.0f) {
@@ -1481,8 +1515,11 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
   }
   // min-p after top-p (as on the candidate path)
   const double c2m = kLog2e / (double)t;
+  const bool minp_on = rp.minp > 0.0f;   // uniform: the weight is computed only when min-p is on
   auto keep = [&](uint32_t rk, uint32_t idx) {
-    return sel_member(sp, rk, idx) && (rp.minp <= 0.0f || weight32(rk, m, c2m) >= rp.minp);
+    bool in = sel_member(sp, rk, idx);
+    if (minp_on) in = in && weight32(rk, m, c2m) >= rp.minp;
+    return in;
   };
   if (MODE == kModeTopp) {
     if (rp.minp > 0.0f) {
@@ -1523,7 +1560,9 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       for (int u = 0; u < kPer; ++u) {
         const uint32_t i = s0 + (uint32_t)(u * kRT) + threadIdx.x;
         cur[u] = f2key(__uint_as_float(cur[u]));
-        bal[u] = __ballot(i < V && sel_member(sk, cur[u], i) && keep(cur[u], i));
+        bool mem = i < V && sel_member(sk, cur[u], i) && sel_member(sp, cur[u], i);
+        if (minp_on) mem = mem && weight32(cur[u], m, c2m) >= rp.minp;
+        bal[u] = __ballot(mem);
         tot += (uint32_t)__popcll(bal[u]);
       }
       if (tot) {   // wave-uniform: one reservation per wave and slab
