@@ -8,9 +8,11 @@ Parity pins (see tests/test_oracle_*.py): brute-force ranks and subset enumerati
 V <= 16, closed forms (all-equal rows, two-token rows, dominant tokens, p = 1), library
 cross-checks (numpy stable argsort, scipy logsumexp), an independent Philox4x32
 implementation (Triton's CPU interpreter, when importable), the inverse Gumbel CDF, and
-chi-square / z tests of the sampling law. No function here is "parity unpinned".
+chi-square / z tests of the sampling law; for the rejection sampler, hand-worked
+trajectories with injected random words and the law of the truncated distribution. No function here is "parity unpinned".
 """
 from .philox import philox4x32, philox4x32_np, seed_key, token_words
+from .rejection import RejectionResult, rejection_sample_row, rejection_sample_rows, round_word
 from .sampler import (
     STATUS_BAD_K,
     STATUS_BAD_MINP,
