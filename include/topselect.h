@@ -205,6 +205,42 @@ int ts_sample_rows_minp(const float* logits, int64_t rows, int64_t vocab, int64_
                         int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ts_sample_rows_rejection -- sorting-free sampling by dual-pivot rejection ([REJ] mlxcel
+ * issue #901 "Sorting-free top-k/top-p/min-p sampling with dual-pivot rejection kernels",
+ * "Background": per round one candidate from a CDF scan over the tokens above the lower
+ * bound, a second pivot halfway to the upper bound, counts and masses above both, accept or
+ * shrink; "Task" item 2: a round cap with an exact fallback for the row).
+ *
+ * Support of row r: the first n tokens of the row ordering, n = min(k, n_p, n_m), where n_p
+ * is the shortest prefix whose probability mass reaches top_p[r] over the WHOLE row (the
+ * joint filter: top-k and top-p tested together against the full distribution, unlike
+ * ts_sample_rows, whose top-p is taken over the top-k set) and n_m counts the tokens with
+ * exp((x - max) / T) >= min_p[r]. The token is drawn with probability proportional to
+ * exp((x - max) / T) on the support (masses as integers floor(w * 2^S), S = 63 - bitlen(vocab);
+ * each round's random word is word 0 of Philox4x32-10 keyed by seed[r] at counter
+ * (round, r, 1, 0), drawn against floor(word * mass / 2^32)). Equal logits rank by id.
+ *   top_k, top_p, temperature, min_p   [rows] device arrays or NULL (off / 1 / 1 / 0);
+ *                 T == 0 is greedy (the first token of the ordering).
+ *   seed        [rows] u64, required.
+ *   max_rounds  rejection rounds before the fallback, in [0, 64] (else TS_ERR_INVALID_ARG);
+ *               a row that reaches it finds its support's last token by bisection over the
+ *               row ordering and draws once over the support (the word of counter
+ *               (max_rounds, r, 1, 0)).
+ *   out_token   [rows] i32, required: the token, -1 for rejected rows.
+ *   out_rounds  [rows] i32 or NULL: the accepting round (1-based), 0 for greedy or rejected
+ *               rows, -1 when the fallback drew the token.
+ *   row_status  [rows] i32 or NULL: as for ts_sample_rows_minp.
+ * Needs no workspace: one 1024-thread workgroup per row reads the row from global memory
+ * once per pass (two passes, then one per round). Weights are fp32-accurate (about 1.6e-7
+ * relative), so a draw within that of a mass boundary may fall on either side.
+ */
+int ts_sample_rows_rejection(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                             const int32_t* top_k, const float* top_p, const float* temperature,
+                             const float* min_p, const uint64_t* seed, int32_t max_rounds,
+                             int32_t* out_token, int32_t* out_rounds, int32_t* row_status,
+                             void* stream);
+
+/*
  * Diagnostic: the noise the sampler uses. For each tokens[j] of row `row` under `seed`,
  * writes the Philox word, u and g (all device arrays of n entries; any output may be NULL).
  */

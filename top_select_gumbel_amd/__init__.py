@@ -37,7 +37,7 @@ TS_KNOB_FORCE_EXACT = 2
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",
-    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_topp_mask_minp.restype = c.c_int
         lib.ts_sample_rows_minp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_sample_rows_minp.restype = c.c_int
+        lib.ts_sample_rows_rejection.restype = c.c_int
+        lib.ts_sample_rows_rejection.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         lib.ts_gumbel_noise.argtypes = [c.c_uint64, i32, vp, i64, vp, vp, vp, vp]
         lib.ts_gumbel_noise.restype = c.c_int
         lib.ts_debug_set.argtypes = [c.c_int, i64]
@@ -284,6 +286,28 @@ def ts_sample_rows_minp(logits, top_k, top_p, temperature, min_p, seed):
                                    _ptr(temperature), _ptr(min_p), _ptr(seed), _ptr(tok), _ptr(st),
                                    _ptr(ws), ws.numel(), _stream()))
     return tok, st
+
+
+def ts_sample_rows_rejection(logits, top_k, top_p, temperature, min_p, seed, max_rounds: int = 32):
+    """Dual-pivot rejection sampling: returns (tokens int32, rounds int32, status int32), each
+    [rows]; rounds is the accepting round (1-based), 0 for greedy or rejected rows, -1 when the
+    row reached max_rounds and took the exact fallback draw."""
+    import torch
+    lib = load_library()
+    rows, v, stride = _rows_view(logits)
+    top_k = _opt(top_k, "torch.int32", rows)
+    top_p = _opt(top_p, "torch.float32", rows)
+    temperature = _opt(temperature, "torch.float32", rows)
+    min_p = _opt(min_p, "torch.float32", rows)
+    if seed is None or str(seed.dtype) not in ("torch.uint64", "torch.int64") or seed.numel() != rows:
+        raise TopSelectError("seed must be a uint64/int64 device tensor with one entry per row")
+    tok = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    rnd = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    st = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _check(lib.ts_sample_rows_rejection(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
+                                        _ptr(temperature), _ptr(min_p), _ptr(seed), int(max_rounds),
+                                        _ptr(tok), _ptr(rnd), _ptr(st), _stream()))
+    return tok, rnd, st
 
 
 def ts_gumbel_noise(seed: int, row: int, tokens):

@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "topselect.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("topselect.hip", "rejection.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopselect.so")
 
@@ -38,7 +38,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile libtopselect.so (always recompiles). Returns the library path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, "-I", os.path.join(PKG, "csrc"), SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, "-I", os.path.join(PKG, "csrc"), *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -54,6 +54,7 @@
 
 #include "topselect.h"
 #include "ts_device.hpp"
+#include "ts_host.hpp"
 
 using namespace tsd;
 
@@ -677,31 +678,6 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
 
 // ------------------------------------------------------------------ misc helpers
 
-constexpr double kLog2e = 1.4426950408889634;   // log2(e)
-
-// Unnormalized weight exp((x - m) / T) of a key, about 1.5e-7 relative: the base-2 exponent
-// z = (x - m) * log2(e) / T is formed in binary64 (x - m exact, c2 = log2(e) / T rounded
-// once), split into integer and fraction, and only 2^fraction is evaluated in fp32.
-// -inf logits (and weights below 2^-200) give 0.
-__device__ __forceinline__ float weight32(uint32_t key, float m, double c2) {
-  const double z = ((double)key2f(key) - (double)m) * c2;   // <= 0
-  if (!(z > -200.0)) return 0.0f;
-  const double n = floor(z);
-  return ldexpf(exp2f((float)(z - n)), (int)n);
-}
-
-// ceil(p * Z) for p = fp32 in (0, 1) and a fixed-point total Z: with p = mant * 2^-psh
-// (mant < 2^24) the product is exact in 128 bits.
-__device__ __forceinline__ uint64_t topp_target(float p, uint64_t z) {
-  int pe;
-  const float pf = frexpf(p, &pe);                          // p = pf * 2^pe, pf in [0.5, 1)
-  const uint64_t mant = (uint64_t)ldexpf(pf, 24);
-  const int psh = 24 - pe;                                  // > 24 since p < 1
-  const unsigned __int128 prod = (unsigned __int128)mant * z;
-  return psh >= 128 ? (prod != 0 ? 1ull : 0ull)
-                    : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
-}
-
 __device__ __forceinline__ float gumbel_score(uint32_t key, uint32_t idx, float m, float t,
                                               uint32_t r, uint32_t k0, uint32_t k1) {
   const uint4 w = philox4x32_10(idx >> 2, r, k0, k1);
@@ -709,7 +685,6 @@ __device__ __forceinline__ float gumbel_score(uint32_t key, uint32_t idx, float 
   return (key2f(key) - m) / t + g;
 }
 
-__device__ __forceinline__ int bitlen(uint32_t n) { return n ? 32 - __clz((int)n) : 0; }
 
 // Ordered emission over an id-ordered source, E consecutive items per thread per tile (all
 // loads of a tile are issued before any is used); out(pos, idx) writes selected item `idx`
@@ -2015,7 +1990,12 @@ __global__ void ts_noise_kernel(uint64_t seed, int32_t row, const int32_t* token
   if (out_g) out_g[j] = gumbel_from_uniform(u);
 }
 
+}  // namespace
+
 // ================================================================== host side
+// Error reporting and the device check, shared with the other sources of the library.
+namespace tsh {
+
 thread_local std::string g_last_error;
 
 int fail(int code, const char* fmt, ...) {
@@ -2027,9 +2007,6 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
-
-std::atomic<int64_t> g_knob_chunk{0};
-std::atomic<int64_t> g_knob_exact{0};
 
 struct DevProps {
   bool probed = false;
@@ -2057,6 +2034,18 @@ int check_device(int* dev_out) {
   *dev_out = dev;
   return TS_OK;
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace tsh
+
+namespace {
+
+using tsh::check_device;
+using tsh::fail;
+
+std::atomic<int64_t> g_knob_chunk{0};
+std::atomic<int64_t> g_knob_exact{0};
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
@@ -2303,6 +2292,6 @@ const char* ts_status_string(int status) {
   }
 }
 
-const char* ts_last_error(void) { return g_last_error.c_str(); }
+const char* ts_last_error(void) { return tsh::last_error(); }
 
 }  // extern "C"

@@ -252,9 +252,10 @@ __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11):
 // ten rounds of the 4x32 bijection with multipliers 0xD2511F53 / 0xCD9E8D57 and Weyl
-// key increments 0x9E3779B9 / 0xBB67AE85. Counter (c0, c1, 0, 0), key (k0, k1).
-__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
-  uint32_t c2 = 0u, c3 = 0u;
+// key increments 0x9E3779B9 / 0xBB67AE85. Counter (c0, c1, c2, 0), key (k0, k1).
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1,
+                                               uint32_t c2_in = 0u) {
+  uint32_t c2 = c2_in, c3 = 0u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
@@ -282,5 +283,34 @@ __device__ __forceinline__ float gumbel_from_uniform(float u) { return -logf(-lo
 // totals do not depend on the order of the additions: a weight w in [0, 1] counts as
 // floor(w * 2^S), S chosen per row so that n weights cannot overflow (S = 63 - bitlen(n)).
 __device__ __forceinline__ uint64_t mass1_of(double w, int s) { return (uint64_t)ldexp(w, s); }
+
+
+// ---------------------------------------------------------------- weights
+constexpr double kLog2e = 1.4426950408889634;   // log2(e)
+
+// Unnormalized weight exp((x - m) / T) of a key, about 1.5e-7 relative: the base-2 exponent
+// z = (x - m) * log2(e) / T is formed in binary64 (x - m exact, c2 = log2(e) / T rounded
+// once), split into integer and fraction, and only 2^fraction is evaluated in fp32.
+// -inf logits (and weights below 2^-200) give 0.
+__device__ __forceinline__ float weight32(uint32_t key, float m, double c2) {
+  const double z = ((double)key2f(key) - (double)m) * c2;   // <= 0
+  if (!(z > -200.0)) return 0.0f;
+  const double n = floor(z);
+  return ldexpf(exp2f((float)(z - n)), (int)n);
+}
+
+// ceil(p * Z) for p = fp32 in (0, 1) and a fixed-point total Z: with p = mant * 2^-psh
+// (mant < 2^24) the product is exact in 128 bits.
+__device__ __forceinline__ uint64_t topp_target(float p, uint64_t z) {
+  int pe;
+  const float pf = frexpf(p, &pe);                          // p = pf * 2^pe, pf in [0.5, 1)
+  const uint64_t mant = (uint64_t)ldexpf(pf, 24);
+  const int psh = 24 - pe;                                  // > 24 since p < 1
+  const unsigned __int128 prod = (unsigned __int128)mant * z;
+  return psh >= 128 ? (prod != 0 ? 1ull : 0ull)
+                    : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
+}
+
+__device__ __forceinline__ int bitlen(uint32_t n) { return n ? 32 - __clz((int)n) : 0; }
 
 }  // namespace tsd

@@ -40,6 +40,7 @@ class Batch:
     seeds: Optional[np.ndarray] = None  # uint64 [B]
     k_max: int = 0
     name: str = ""
+    min_p: Optional[np.ndarray] = None  # fp32 [B]
 
 
 def _seeds(rng, b):
@@ -160,3 +161,25 @@ def small_random(seed: int, rows: int, vocab: int, k_hi: int, *, scale: float = 
     t = rng.uniform(0.5, 1.5, size=rows).astype(np.float32)
     return Batch(logits=x, k=k, p=p, t=t, seeds=_seeds(rng, rows), k_max=int(k_hi),
                  name=f"random_{rows}x{vocab}")
+
+
+def rejection_mix(seed: int, rows: int, vocab: int, *, tie_levels: int = 0, masked: float = 0.0) -> Batch:
+    """Parameter mix for the rejection sampler: top-k only, top-p only, joint, min-p, off and
+    greedy rows (mlxcel issue #901, "Performance validation": top-k 40, top-p 0.9, min-p
+    0.05 and top-k + top-p); optional exact ties and -inf (masked) tokens."""
+    rng = np.random.default_rng(seed)
+    if tie_levels:
+        x = rng.integers(0, tie_levels, size=(rows, vocab)).astype(np.float64)
+    else:
+        x = rng.standard_normal((rows, vocab)) * 2.0
+    if masked:
+        x[rng.random((rows, vocab)) < masked] = -np.inf
+    x = x.astype(np.float32)
+    kind = np.arange(rows) % 6
+    k = np.where((kind == 0) | (kind == 2), rng.integers(1, 200, size=rows), vocab + 5).astype(np.int32)
+    p = np.where((kind == 1) | (kind == 2), rng.uniform(0.3, 1.0, size=rows), 1.0).astype(np.float32)
+    mp = np.where(kind == 3, rng.uniform(0.01, 0.3, size=rows), 0.0).astype(np.float32)
+    t = rng.uniform(0.5, 1.5, size=rows)
+    t[kind == 5] = 0.0
+    return Batch(logits=x, k=k, p=p, t=t.astype(np.float32), seeds=_seeds(rng, rows),
+                 name=f"rejection_{rows}x{vocab}", min_p=mp)
