@@ -29,9 +29,14 @@ ROTATE = 16                    # 16 x 38.9 MB = 622 MB > 2 x 256 MB
 SRC = os.path.join(ROOT, "top_select_gumbel_amd", "csrc")
 
 
+# The sources of the two kernels of ts_sample_rows (the headline call); the rejection
+# sampler's source is not part of it.
+HEADLINE_SOURCES = ("topselect.hip", "ts_device.hpp")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(SRC)):
+    for name in HEADLINE_SOURCES:
         with open(os.path.join(SRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -91,6 +96,8 @@ OTHER_CONFIGS = {
     "indexer_rows": ("indexer_rows", "topk", 32),
     "indexer_long": ("indexer_long", "topk", 128),
     "indexer_near_uniform": ("indexer_near_uniform", "topk", 900),
+    "decode_rejection": ("decode", "rejection", 16),
+    "decode_topp_only_rejection": ("decode_topp_only", "rejection", 16),
 }
 
 
@@ -111,7 +118,17 @@ def other_config(name, args):
     bufs = [base] + [torch.roll(base, shifts=37 * i, dims=1).contiguous() for i in range(1, rot)]
     st = torch.empty(rows, dtype=torch.int32, device=dev)
     k = torch.from_numpy(b.k).to(dev)
-    if op in ("sample", "sample_logp"):
+    if op == "rejection":
+        p = torch.from_numpy(b.p).to(dev)
+        t = torch.from_numpy(b.t).to(dev)
+        s = torch.from_numpy(b.seeds.view(np.int64)).to(dev)
+        tok = torch.empty(rows, dtype=torch.int32, device=dev)
+        rnd = torch.empty(rows, dtype=torch.int32, device=dev)
+        call = lambda x, h: lib.ts_sample_rows_rejection(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                                                         t.data_ptr(), None, s.data_ptr(), 32, tok.data_ptr(),
+                                                         rnd.data_ptr(), st.data_ptr(), h)
+        cname = "ts_sample_rows_rejection"
+    elif op in ("sample", "sample_logp"):
         p = torch.from_numpy(b.p).to(dev)
         t = torch.from_numpy(b.t).to(dev)
         seeds = b.seeds if b.seeds is not None else wl.heavy_launch_seeds(0, rows)
@@ -166,6 +183,11 @@ def other_config(name, args):
     assert int(st.abs().sum()) == 0, "rows reported errors"
     nbytes = rows * vocab * 4
     med = float(np.median(us))
+    extra = {}
+    if op == "rejection":
+        r = rnd.cpu().numpy()
+        extra = {"rounds_mean": float(r[r > 0].mean()) if (r > 0).any() else 0.0,
+                 "rounds_max": int(r.max()), "fallback_rows": int((r < 0).sum())}
     print(json.dumps({
         "config": name, "op": cname, "rows": rows, "vocab": vocab, "input_buffers": rot,
         "bytes_per_call": nbytes, "steps": args.steps, "warmup": args.warmup,
@@ -176,7 +198,74 @@ def other_config(name, args):
         "effective_GBps_median": nbytes / (med * 1e-6) / 1e9,
         "frac_of_8TBps": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "source_hash": source_hash(),
+        **extra,
     }), flush=True)
+
+
+def rejection_matrix(args):
+    """The sampling matrix of mlxcel issue #901 ("Performance validation"): vocab {32000,
+    65536, 151936} x batch {1, 4, 8} x filter {top-k 40, top-p 0.9, min-p 0.05, top-k 40 +
+    top-p 0.9}, T = 1, the exact sampler (ts_sample_rows_minp) against the rejection sampler
+    (ts_sample_rows_rejection). Inputs rotate over 512 MB so every call reads HBM. One JSON
+    line per cell (median kernel time per call)."""
+    import numpy as np
+    import torch
+
+    import top_select_gumbel_amd as ts
+    from top_select_gumbel_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    lib = ts.load_library()
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    filters = {"top-k 40": (40, 1.0, 0.0), "top-p 0.9": (None, 0.9, 0.0), "min-p 0.05": (None, 1.0, 0.05),
+               "top-k 40 + top-p 0.9": (40, 0.9, 0.0)}
+
+    def timed(call, ptrs, n):
+        for i in range(20):
+            call(ptrs[i % len(ptrs)])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            rc = call(ptrs[i % len(ptrs)])
+            ev[i][1].record(stream)
+            if rc:
+                raise RuntimeError(ts.ts_last_error())
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(e) for a, e in ev])) * 1e3
+
+    for vocab in (32000, 65536, 151936):
+        for rows in (1, 4, 8):
+            b = wl.decode(seed=2, rows=rows, vocab=vocab)
+            rot = max(1, (512 << 20) // (rows * vocab * 4))
+            big = torch.from_numpy(np.tile(b.logits.ravel(), rot)).to(dev)
+            ptrs = [big.data_ptr() + i * rows * vocab * 4 for i in range(rot)]
+            s = torch.from_numpy(b.seeds.view(np.int64)).to(dev)
+            t = torch.ones(rows, dtype=torch.float32, device=dev)
+            tok = torch.empty(rows, dtype=torch.int32, device=dev)
+            rnd = torch.empty(rows, dtype=torch.int32, device=dev)
+            st = torch.empty(rows, dtype=torch.int32, device=dev)
+            nb = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, rows, vocab, 0)
+            ws = ts.workspace(nb, dev)
+            for fname, (kk, pp, mm) in filters.items():
+                k = torch.full((rows,), kk if kk else vocab, dtype=torch.int32, device=dev)
+                p = torch.full((rows,), pp, dtype=torch.float32, device=dev)
+                mp = torch.full((rows,), mm, dtype=torch.float32, device=dev)
+                exact = lambda x: lib.ts_sample_rows_minp(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                                                          t.data_ptr(), mp.data_ptr(), s.data_ptr(), tok.data_ptr(),
+                                                          st.data_ptr(), ws.data_ptr(), ws.numel(), h)
+                rej = lambda x: lib.ts_sample_rows_rejection(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                                                             t.data_ptr(), mp.data_ptr(), s.data_ptr(), 32,
+                                                             tok.data_ptr(), rnd.data_ptr(), st.data_ptr(), h)
+                us_exact = timed(exact, ptrs, args.steps)
+                us_rej = timed(rej, ptrs, args.steps)
+                r = rnd.cpu().numpy()
+                assert int(st.abs().sum()) == 0, "rows reported errors"
+                print(json.dumps({"config": "rejection_matrix", "vocab": vocab, "rows": rows, "filter": fname,
+                                  "exact_us_median": us_exact, "rejection_us_median": us_rej,
+                                  "rejection_over_exact": us_rej / us_exact,
+                                  "rounds_last_call": r.tolist()}), flush=True)
+            del big
 
 
 def main():
@@ -186,7 +275,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm-only", action="store_true")
-    ap.add_argument("--config", default="decode", choices=["decode"] + sorted(OTHER_CONFIGS),
+    ap.add_argument("--config", default="decode", choices=["decode", "rejection_matrix"] + sorted(OTHER_CONFIGS),
                     help="decode (the headline line) or one of the other workloads, timed alone")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -195,6 +284,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "rejection_matrix":
+        rejection_matrix(args)
+        return
     if args.config != "decode":
         other_config(args.config, args)
         return

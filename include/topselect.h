@@ -246,6 +246,12 @@ int ts_sample_rows_rejection(const float* logits, int64_t rows, int64_t vocab, i
  */
 int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n,
                     uint32_t* out_word, float* out_u, float* out_g, void* stream);
+/*
+ * Diagnostic: the sampler's word -> (u, g) map on given 32-bit words (device arrays of n
+ * entries; either output may be NULL): u = fp32(word * 2^-32) clamped to [2^-32, 1 - 2^-24]
+ * and g = -log(-log1p(-u)) ([GUMBEL] "implementation breakdown"), as ts_sample_rows uses them.
+ */
+int ts_noise_transform(const uint32_t* words, int64_t n, float* out_u, float* out_g, void* stream);
 
 /*
  * Test-only, bit-neutral path forcing (process-wide; not thread-safe). Knobs:

@@ -37,7 +37,7 @@ TS_KNOB_FORCE_EXACT = 2
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",
-    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_noise_transform", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -83,6 +83,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_sample_rows_rejection.restype = c.c_int
         lib.ts_sample_rows_rejection.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         lib.ts_gumbel_noise.argtypes = [c.c_uint64, i32, vp, i64, vp, vp, vp, vp]
+        lib.ts_noise_transform.restype = c.c_int
+        lib.ts_noise_transform.argtypes = [vp, i64, vp, vp, vp]
         lib.ts_gumbel_noise.restype = c.c_int
         lib.ts_debug_set.argtypes = [c.c_int, i64]
         lib.ts_debug_set.restype = i64
@@ -321,6 +323,17 @@ def ts_gumbel_noise(seed: int, row: int, tokens):
     _check(lib.ts_gumbel_noise(int(seed) & 0xFFFFFFFFFFFFFFFF, int(row), _ptr(tokens), n, _ptr(word),
                                _ptr(u), _ptr(g), _stream()))
     return word, u, g
+
+
+def ts_noise_transform(words):
+    """The sampler's (u, g) for given 32-bit words (an int32/uint32 device tensor)."""
+    import torch
+    lib = load_library()
+    n = words.numel()
+    u = torch.empty(n, dtype=torch.float32, device=words.device)
+    g = torch.empty(n, dtype=torch.float32, device=words.device)
+    _check(lib.ts_noise_transform(_ptr(words), n, _ptr(u), _ptr(g), _stream()))
+    return u, g
 
 
 def ts_debug_set(knob: int, value: int) -> int:

@@ -1990,6 +1990,14 @@ __global__ void ts_noise_kernel(uint64_t seed, int32_t row, const int32_t* token
   if (out_g) out_g[j] = gumbel_from_uniform(u);
 }
 
+__global__ void ts_noise_words_kernel(const uint32_t* words, int64_t n, float* out_u, float* out_g) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const float u = uniform_from_word(words[j]);
+  if (out_u) out_u[j] = u;
+  if (out_g) out_g[j] = gumbel_from_uniform(u);
+}
+
 }  // namespace
 
 // ================================================================== host side
@@ -2260,6 +2268,21 @@ int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n
   const unsigned blocks = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(ts_noise_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, seed, row,
                      tokens, n, out_word, out_u, out_g);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "noise launch failed: %s", hipGetErrorString(e));
+  return TS_OK;
+}
+
+int ts_noise_transform(const uint32_t* words, int64_t n, float* out_u, float* out_g, void* stream) {
+  if (n < 0) return fail(TS_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return TS_OK;
+  if (!words) return fail(TS_ERR_INVALID_ARG, "words is NULL");
+  if (n > ((int64_t)1 << 40)) return fail(TS_ERR_INVALID_ARG, "n too large");
+  int dev;
+  int rc = check_device(&dev);
+  if (rc != TS_OK) return rc;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(ts_noise_words_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, words, n, out_u, out_g);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "noise launch failed: %s", hipGetErrorString(e));
   return TS_OK;

@@ -275,8 +275,20 @@ __device__ __forceinline__ float uniform_from_word(uint32_t w) {
   const float u = (float)w * 0x1p-32f;
   return fminf(fmaxf(u, 0x1p-32f), 1.0f - 0x1p-24f);
 }
-// Gumbel noise with the log1p(-u) transform: the large-noise tail maps to u -> 0.
-__device__ __forceinline__ float gumbel_from_uniform(float u) { return -logf(-log1pf(-u)); }
+// Gumbel noise g = -log(E), E = -log1p(-u): the large-noise tail maps to u -> 0.
+// log1p(-u) by Goldberg's compensation ("What every computer scientist should know about
+// floating-point arithmetic", ACM Computing Surveys 1991, theorem 4): with y = fl(1 - u) and
+// d = 1 - y (exact), log1p(-u) = log(y) * u / d, and -u itself when y == 1; the rounding of y
+// cancels in the ratio. Both logarithms come from the hardware base-2 logarithm (v_log_f32,
+// normal inputs only here: y >= 2^-24, E >= 2^-32) scaled by ln 2. Error of g within 1e-6 plus
+// two fp32 ulps of g over the whole clamped range of u (checked on the GPU against binary64).
+__device__ __forceinline__ float gumbel_from_uniform(float u) {
+  constexpr float kLn2f = 0.693147180559945309f;
+  const float y = 1.0f - u;
+  const float d = 1.0f - y;
+  const float e = (y == 1.0f) ? u : (-__builtin_amdgcn_logf(y) * kLn2f) * (u * __builtin_amdgcn_rcpf(d));
+  return -__builtin_amdgcn_logf(e) * kLn2f;
+}
 
 // ---------------------------------------------------------------- fixed-point mass
 // Probability mass is summed exactly in unsigned 64-bit fixed point so that histograms and
