@@ -127,6 +127,7 @@ struct Params {
   int32_t cap_w;
   int32_t xcd_map;
   int32_t force_exact;
+  int32_t direct;              // rows of <= kLdsCand logits: the row kernel alone, row in LDS
   int32_t* out_idx;
   int32_t* out_kept;
   uint8_t* out_mask;
@@ -1722,6 +1723,32 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
   return nf;
 }
 
+// Top-k select output of a certified candidate selection: the selected ids ascending (or in
+// the row ordering for TS_ORDER_VALUE), shifted by the row's offset, then -1 padding.
+__device__ __forceinline__ void emit_topk_cand(const Params& P, const RowPlan& rp, int r, uint32_t ntot,
+                                               const Sel& sk, Smem& sm) {
+  int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
+  const uint32_t kmx = (uint32_t)P.k_max;
+  const int32_t off = P.offsets ? P.offsets[r] : 0;
+  if (P.order == TS_ORDER_VALUE) {
+    // K (<= kFastK items) compacted, then sorted in the free mass histogram
+    const uint32_t nk = min(append_members(sm.ckey, sm.cidx, ntot,
+                                           [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                                           sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
+                            (uint32_t)kFastK);
+    uint64_t* a = reinterpret_cast<uint64_t*>(sm.mhi);
+    for (uint32_t i = threadIdx.x; i < nk; i += kRT) a[i] = ((uint64_t)sm.kkey[i] << 32) | (uint32_t)~sm.kidx[i];
+    emit_value_order(a, nk, (uint32_t)kDBins, orow, kmx, off);
+  } else {
+    uint32_t run = 0;
+    emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
+                    [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
+                    [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = off + (int32_t)idx; },
+                    run, sm);
+  }
+  for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   __shared__ Smem sm;
@@ -1732,18 +1759,37 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   const int r = P.xcd_map ? (b & 7) * (P.rows >> 3) + (b >> 3) : b;
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
-  // Aggregate the wave summaries. Their loads are issued first; the row parameters and the
-  // seed load while they are in flight. Counts go to LDS for the slice offsets.
   uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
-  for (int i = threadIdx.x; i < nseg; i += kRT) {
-    const WaveInfo wi = inf[i];
-    flags |= wi.flags;
-    kmax = max(kmax, wi.kmax);
-    thr_max = max(thr_max, wi.thr);
-    cmin = min(cmin, wi.thr);
-    if (i < kMaxSeg) sm.segoff[i] = wi.count;
+  RowPlan rp;
+  if (P.direct) {
+    // The whole row is the candidate set: its keys and ids go straight to LDS (no stream
+    // kernel ran). Every element is a candidate, so the certification below always holds
+    // (thr_max = 0); cmin is the row's smallest key.
+    rp = plan_row(P, MODE, r);
+    const float* row = P.x + (int64_t)r * P.stride;
+#pragma unroll 4
+    for (int i = threadIdx.x; i < rp.n; i += kRT) {
+      const float v = row[i];
+      const uint32_t key = f2key(v);
+      flags |= (v != v) ? kFlagNan : 0u;
+      kmax = max(kmax, key);
+      cmin = min(cmin, key);
+      sm.ckey[i] = key;
+      sm.cidx[i] = (uint32_t)i;
+    }
+  } else {
+    // Aggregate the wave summaries. Their loads are issued first; the row parameters and
+    // the seed load while they are in flight. Counts go to LDS for the slice offsets.
+    for (int i = threadIdx.x; i < nseg; i += kRT) {
+      const WaveInfo wi = inf[i];
+      flags |= wi.flags;
+      kmax = max(kmax, wi.kmax);
+      thr_max = max(thr_max, wi.thr);
+      cmin = min(cmin, wi.thr);
+      if (i < kMaxSeg) sm.segoff[i] = wi.count;
+    }
+    rp = plan_row(P, MODE, r);
   }
-  const RowPlan rp = plan_row(P, MODE, r);
   const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
   // zero the histograms (each select leaves them zero again) and the small-bin counter
   if (threadIdx.x == 0) sm.bcount = 0;
@@ -1767,7 +1813,12 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   double lse = 0.0;
   if (MODE == kModeSample && P.wsum) {
     double zpart = 0.0;
-    if (st == TS_ROW_OK && rp.t > 0.0f) {
+    if (st == TS_ROW_OK && rp.t > 0.0f && P.direct) {
+      // the row is in LDS: S directly, exp(y) = 2^(y log2 e) in fp32, binary64 accumulation
+      const float m_f = key2f(kmax);
+      const float c2f = (float)(1.4426950408889634 / (double)rp.t);
+      for (int i = threadIdx.x; i < rp.n; i += kRT) zpart += (double)exp2f((key2f(sm.ckey[i]) - m_f) * c2f);
+    } else if (st == TS_ROW_OK && rp.t > 0.0f) {
       const double m = (double)key2f(kmax);
       for (int i = threadIdx.x; i < nseg; i += kRT) {
         const uint32_t kw = inf[i].kmax;
@@ -1778,8 +1829,15 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     lse = (double)key2f(kmax) / (double)rp.t + log(z);
   }
 
+  if (MODE == kModeTopp && P.direct && P.out_mask) {
+    // no stream kernel wrote the mask row: all ones for a full row, else zeros (the kept
+    // tokens are marked below, after every zero has landed)
+    fill_bytes_nt<kRT>(P.out_mask + (int64_t)r * P.V, P.V,
+                       (st == TS_ROW_OK && rp.path == kPathFull) ? (uint8_t)1 : (uint8_t)0);
+    bar_all();
+  }
   if (st != TS_ROW_OK) {
-    if (MODE == kModeTopp && rp.path == kPathFull && P.out_mask) {
+    if (MODE == kModeTopp && rp.path == kPathFull && P.out_mask && !P.direct) {
       fill_bytes_nt<kRT>(P.out_mask + (int64_t)r * P.V, P.V, 0);   // chunks had written ones
     }
     if (MODE == kModeTopk) {
@@ -1799,9 +1857,14 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   if (path == kPathGreedy) {
     // slices are in id order: the lowest id holding the row maximum
     uint32_t idx = 0xFFFFFFFFu;
-    for (int i = threadIdx.x; i < nseg; i += kRT) {
-      const WaveInfo wi = inf[i];
-      if (wi.kmax == kmax) idx = min(idx, wi.kmax_idx);
+    if (P.direct) {
+      for (int i = threadIdx.x; i < rp.n; i += kRT)
+        if (sm.ckey[i] == kmax) idx = min(idx, (uint32_t)i);
+    } else {
+      for (int i = threadIdx.x; i < nseg; i += kRT) {
+        const WaveInfo wi = inf[i];
+        if (wi.kmax == kmax) idx = min(idx, wi.kmax_idx);
+      }
     }
     idx = block_min_u32<kRW>(idx, sm.red);
     if (MODE == kModeTopp) {
@@ -1824,10 +1887,18 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       const float m = key2f(kmax);
       float bs = -INFINITY;
       int32_t bi = 0x7FFFFFFF;
-      for (int i = threadIdx.x; i < nseg; i += kRT) {
-        const WaveInfo wi = inf[i];
-        const float adj = wi.best_s + (key2f(wi.kmax) - m) / rp.t;
-        if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
+      if (P.direct) {
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        for (int i = threadIdx.x; i < rp.n; i += kRT) {
+          const float sc = gumbel_score(sm.ckey[i], (uint32_t)i, m, rp.t, (uint32_t)r, k0, k1);
+          if (sc > bs) { bs = sc; bi = i; }   // ids rise along a thread's elements
+        }
+      } else {
+        for (int i = threadIdx.x; i < nseg; i += kRT) {
+          const WaveInfo wi = inf[i];
+          const float adj = wi.best_s + (key2f(wi.kmax) - m) / rp.t;
+          if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
+        }
       }
       bi = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
       if (threadIdx.x == 0) {
@@ -1840,7 +1911,25 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
 
   // the smallest key the exact path must consider (a lower bound of the row's k-th key)
   uint32_t kfloor = kKeyNegInf;
-  if (path == kPathCand && nseg <= kMaxSeg) {
+  if (path == kPathCand && P.direct) {
+    const uint32_t ntot = (uint32_t)rp.n;
+    if (ntot && !P.force_exact) {
+      const uint32_t ke = (uint32_t)rp.k_eff;
+      auto vis = [&](auto f) { lds_for(sm.ckey, sm.cidx, ntot, f); };
+      Sel sk = sel_all();
+      uint32_t min_sel = cmin;
+      if (ntot > ke) {
+        sk = select_topk(vis, ke, ntot, kmax, cmin, 0u, (uint32_t)(P.V - 1), sm, false);
+        min_sel = shl(sk.prefix, sk.lo);
+      }
+      if (MODE == kModeTopk) {
+        emit_topk_cand(P, rp, r, ntot, sk, sm);
+        return;
+      }
+      finish_cand<MODE>(P, rp, r, kmax, max(cmin, min_sel), seed, ntot, sk, sm, lse);
+      return;
+    }
+  } else if (path == kPathCand && nseg <= kMaxSeg) {
     const uint32_t ke = (uint32_t)rp.k_eff;
     // exclusive prefix of the slice counts (kSegPT consecutive slices per thread): the
     // candidates' flat, id-ordered index space
@@ -1941,26 +2030,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       // was published by its wave, so the candidates' top-k is the row's top-k.
       if (min_sel >= thr_max) {
         if (MODE == kModeTopk) {
-          int32_t* orow = P.out_idx + (int64_t)r * P.k_max;
-          const uint32_t kmx = (uint32_t)P.k_max;
-          const int32_t off = P.offsets ? P.offsets[r] : 0;
-          if (P.order == TS_ORDER_VALUE) {
-            // K (<= kFastK items) compacted, then sorted in the free mass histogram
-            const uint32_t nk = min(append_members(sm.ckey, sm.cidx, ntot,
-                                                   [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                                                   sm.kkey, sm.kidx, (uint32_t)kFastK, 0, sm),
-                                    (uint32_t)kFastK);
-            uint64_t* a = reinterpret_cast<uint64_t*>(sm.mhi);
-            for (uint32_t i = threadIdx.x; i < nk; i += kRT) a[i] = ((uint64_t)sm.kkey[i] << 32) | (uint32_t)~sm.kidx[i];
-            emit_value_order(a, nk, (uint32_t)kDBins, orow, kmx, off);
-          } else {
-            uint32_t run = 0;
-            emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
-                            [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
-                            [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = off + (int32_t)idx; },
-                            run, sm);
-          }
-          for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
+          emit_topk_cand(P, rp, r, ntot, sk, sm);
           return;
         }
         finish_cand<MODE>(P, rp, r, kmax, max(lo_key, min_sel), seed, ntot, sk, sm, lse);
@@ -2054,6 +2124,7 @@ using tsh::fail;
 
 std::atomic<int64_t> g_knob_chunk{0};
 std::atomic<int64_t> g_knob_exact{0};
+std::atomic<int64_t> g_knob_direct{1};
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
@@ -2132,6 +2203,8 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.cap_w = (int32_t)pl.cap_w;
   P.xcd_map = (pl.chunks > 1 && rows % 8 == 0) ? 1 : 0;
   P.force_exact = (int32_t)g_knob_exact.load();
+  // Rows that fit the row kernel's LDS skip the stream kernel (unless a chunk size is forced).
+  P.direct = (V <= kLdsCand && g_knob_chunk.load() == 0 && g_knob_direct.load() != 0) ? 1 : 0;
   P.out_idx = out_idx;
   P.out_kept = out_kept;
   P.out_mask = out_mask;
@@ -2144,9 +2217,12 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.cand = reinterpret_cast<uint2*>(w + pl.off_cand);
   P.wsum = (out_logp || out_lse) ? reinterpret_cast<double*>(w + pl.off_wsum) : nullptr;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(ts_stream_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "stream kernel launch failed: %s", hipGetErrorString(e));
+  hipError_t e;
+  if (!P.direct) {
+    hipLaunchKernelGGL(ts_stream_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "stream kernel launch failed: %s", hipGetErrorString(e));
+  }
   hipLaunchKernelGGL(ts_row_kernel<MODE>, dim3((unsigned)rows), dim3(kRT), 0, s, P);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "row kernel launch failed: %s", hipGetErrorString(e));
@@ -2295,6 +2371,7 @@ int64_t ts_debug_set(int knob, int64_t value) {
       return g_knob_chunk.exchange(value);
     }
     case TS_KNOB_FORCE_EXACT: return g_knob_exact.exchange(value ? 1 : 0);
+    case TS_KNOB_DIRECT: return g_knob_direct.exchange(value ? 1 : 0);
     default: return -1;
   }
 }
