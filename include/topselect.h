@@ -260,7 +260,7 @@ int ts_noise_transform(const uint32_t* words, int64_t n, float* out_u, float* ou
  *                         over workgroups. Also changes ts_workspace_bytes.
  *   TS_KNOB_FORCE_EXACT   1 = every top-k / top-p row takes the exact row-streaming path of
  *                         the row kernel instead of the certified candidate path.
- *   TS_KNOB_DIRECT        1 (default) = rows of at most 8192 logits run in the row kernel
+ *   TS_KNOB_DIRECT        1 (default) = rows of at most 12288 logits run in the row kernel
  *                         alone, the row loaded straight into its LDS (one launch instead of
  *                         two); 0 = such rows also take the stream kernel. A forced chunk size
  *                         also turns it off.

@@ -1,8 +1,8 @@
-"""Rows of at most 8192 logits run in the row kernel alone (the row loaded into LDS; no
+"""Rows of at most 12288 logits run in the row kernel alone (the row loaded into LDS; no
 stream kernel). The same inputs through the two-kernel path (TS_KNOB_DIRECT = 0) must give
 the same top-k ids, kept counts, masks and tokens, and both must match the oracle (top-k
 bit-exact, top-p counts, sampled ids outside near-ties). Covers the 4 x 1024 and 200 x 16
-rows of the small configuration, ragged lengths, the 8192 boundary and greedy / full-row /
+rows of the small configuration, ragged lengths, 8192- and 12288-logit rows and greedy / full-row /
 rejected rows.
 """
 import numpy as np
@@ -51,9 +51,10 @@ def batches():
     b.logits[3, 77] = np.nan                         # rejected row
     yield b
     yield wl.small_random(52, 16, 3000, 1500, tie_levels=5)
+    yield wl.small_random(53, 12, 12288, 2048, scale=1.5)
 
 
-@pytest.mark.parametrize("idx", range(4))
+@pytest.mark.parametrize("idx", range(5))
 def test_direct_matches_two_kernel_path_and_oracle(idx):
     b = list(batches())[idx]
     x = b.logits

@@ -187,8 +187,10 @@ def test_topk_indexer_long_and_near_uniform():
 
 
 def test_topk_long_rows_global_candidates():
-    # More candidates than LDS holds (1M-element rows, k=2048): row 0 takes the filtered
-    # gather from the slices in global memory; row 1 has 40000 ties at its maximum, so every
+    # 1M-element rows, k=2048. Row 0 publishes about 9,700 candidates: they fit in LDS with
+    # the automatic 8192-logit chunks; with 4096-logit chunks (twice the workgroups, so twice
+    # the per-workgroup safety margins) about 14,000 do not, and the row takes the filtered
+    # gather from the slices in global memory. Row 1 has 40000 ties at its maximum, so every
     # candidate key is equal and the first k by id are taken; row 2 puts 20000 items on each
     # of two adjacent fp32 values, the filtered set is still too large and the row takes the
     # exact path from the smallest workgroup threshold.
@@ -205,6 +207,12 @@ def test_topk_long_rows_global_candidates():
     banner("topk 3x1048576 k=2048: filtered gather, all-equal cut, exact fallback")
     out, st = run_topk(x, k, 2048)
     check_topk(x, k, 2048, out, st, "long")
+    try:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 4096)
+        out2, st2 = run_topk(x, k, 2048)
+    finally:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
+    assert np.array_equal(out2, out) and np.array_equal(st2, st)
 
 
 def test_topk_deterministic_and_path_invariant():
@@ -349,8 +357,9 @@ def test_sample_heavy_rows_match_oracle():
 
 
 def test_topp_and_sample_long_rows_global_candidates():
-    # 1M-element rows whose candidates exceed LDS: top-p and sampling after the filtered
-    # gather from global memory.
+    # 1M-element rows: the candidates fit in LDS with the automatic chunks; with 4096-logit
+    # chunks they exceed it, and top-p and sampling run after the filtered gather from global
+    # memory. Both must give the same bytes.
     rng = np.random.default_rng(92)
     n = 1 << 20
     x = (rng.standard_normal((2, n)) * 2.5).astype(np.float32)
@@ -363,6 +372,13 @@ def test_topp_and_sample_long_rows_global_candidates():
     check_topp(x, k, p, t, kept, mask, st, "long")
     tok, st = run_sample(x, k, p, t, seeds)
     check_samples(x, k, p, t, seeds, tok, st, kept, "long")
+    try:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 4096)
+        kept2, mask2, _ = run_topp(x, k, p, t, want_mask=True)
+        tok2, _ = run_sample(x, k, p, t, seeds)
+    finally:
+        ts.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0)
+    assert np.array_equal(kept2, kept) and np.array_equal(mask2, mask) and np.array_equal(tok2, tok)
 
 
 def test_sample_deterministic_and_path_invariant():

@@ -84,7 +84,9 @@ constexpr int kRW = kRT / 64;
 constexpr int kFastK = 2048;                        // largest k taking the candidate path
 constexpr int kDBits = 11;                          // radix digit of the row selects
 constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel thread
-constexpr int kLdsCand = 8192;                      // candidates the row kernel holds in LDS
+constexpr int kLdsCand = 12288;                     // candidates the row kernel holds in LDS
+constexpr int kSlab = 8192;                         // row elements per row-streaming Gumbel slab
+constexpr int kValueOrderMax = 8192;                // value-ordered top-k: k_max limit (sort size)
 constexpr int kVisU = 4;                            // LDS items per thread per visitor round
 constexpr int kGatherB = 12;
 constexpr uint32_t kSmallBin = 64;                  // boundary bins up to this size are resolved by one wave                        // wave slices per gather batch
@@ -150,7 +152,7 @@ struct RowPlan {
   int32_t bad;
 };
 
-// LDS of the row kernel (about 124 KB; one workgroup per CU)
+// LDS of the row kernel (about 141 KB; one workgroup per CU)
 struct Smem {
   uint32_t ckey[kLdsCand];     // candidates (id order), keys and ids in separate arrays
   uint32_t cidx[kLdsCand];
@@ -1441,14 +1443,14 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       rvis([&](uint32_t rk, uint32_t idx) {
         if (sel_member(sk, rk, idx)) {
           const uint32_t at = atomicAdd(&sm.bcount, 1u);
-          if (at < (uint32_t)(kLdsCand)) a[at] = ((uint64_t)rk << 32) | (uint32_t)~idx;
+          if (at < (uint32_t)kValueOrderMax) a[at] = ((uint64_t)rk << 32) | (uint32_t)~idx;
         }
       });
       bar();
-      const uint32_t nk = min(sm.bcount, (uint32_t)kLdsCand);
+      const uint32_t nk = min(sm.bcount, (uint32_t)kValueOrderMax);
       bar();
       if (threadIdx.x == 0) sm.bcount = 0;
-      emit_value_order(a, nk, (uint32_t)kLdsCand, orow, kmx, off);
+      emit_value_order(a, nk, (uint32_t)kValueOrderMax, orow, kmx, off);
     } else {
       uint32_t run = 0;
       emit_ordered<4>(V, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = f2key(row[i]); idx = i; },
@@ -1512,11 +1514,11 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       });
     }
   } else {
-    // Gumbel-max over P. Per slab of kLdsCand row elements the members of P are compacted
+    // Gumbel-max over P. Per slab of kSlab row elements the members of P are compacted
     // into LDS first, so that noise is drawn only for them (members are scattered: drawing
     // in place would run the generator in nearly every wave for every element).
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    constexpr int kPer = kLdsCand / kRT;
+    constexpr int kPer = kSlab / kRT;
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
     auto load = [&](uint32_t s0, uint32_t (&key)[kPer]) {
@@ -1528,8 +1530,8 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
     };
     uint32_t cur[kPer], nxt[kPer];
     load(0, cur);
-    for (uint32_t s0 = 0; s0 < V; s0 += (uint32_t)kLdsCand) {
-      load(s0 + (uint32_t)kLdsCand, nxt);   // the next slab loads while this one is processed
+    for (uint32_t s0 = 0; s0 < V; s0 += (uint32_t)kSlab) {
+      load(s0 + (uint32_t)kSlab, nxt);   // the next slab loads while this one is processed
       uint64_t bal[kPer];
       uint32_t tot = 0;
 #pragma unroll
@@ -1548,7 +1550,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
           if ((bal[u] >> lane()) & 1ull) {
-            const uint32_t at = wbase + mbcnt(bal[u]);   // < kLdsCand: one slab's members
+            const uint32_t at = wbase + mbcnt(bal[u]);   // < kSlab: one slab's members
             sm.ckey[at] = cur[u];
             sm.cidx[at] = s0 + (uint32_t)(u * kRT) + threadIdx.x;
           }
@@ -2267,8 +2269,8 @@ int ts_topk_select_rows(const float* keys, int64_t rows, int64_t row_len, int64_
   if (k_max < 1) return fail(TS_ERR_INVALID_ARG, "k_max = %d < 1", (int)k_max);
   if (order != TS_ORDER_INDEX && order != TS_ORDER_VALUE)
     return fail(TS_ERR_INVALID_ARG, "order = %d is neither TS_ORDER_INDEX nor TS_ORDER_VALUE", order);
-  if (order == TS_ORDER_VALUE && k_max > kLdsCand)
-    return fail(TS_ERR_INVALID_ARG, "value order supports k_max <= %d (got %d)", kLdsCand, (int)k_max);
+  if (order == TS_ORDER_VALUE && k_max > kValueOrderMax)
+    return fail(TS_ERR_INVALID_ARG, "value order supports k_max <= %d (got %d)", kValueOrderMax, (int)k_max);
   return launch<kModeTopk>(keys, rows, row_len, row_stride, k, k_max, nullptr, nullptr, nullptr,
                            out_idx, nullptr, nullptr, nullptr, row_status, workspace,
                            workspace_bytes, stream, nullptr, nullptr, nullptr, lengths, offsets, order);
