@@ -1018,7 +1018,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t key = f2key(xval(s, e));
-            if (e < nv && (key >> (sh + bits)) == pre) atomicAdd(&sm.hist2[(key >> sh) & ((1u << bits) - 1u)], 1u);
+            // narrow rows put whole waves in one bin: one atomic per wave then
+            if (e < nv && (key >> (sh + bits)) == pre) hist_add(sm.hist2, (key >> sh) & ((1u << bits) - 1u));
           }
         }
         bar();
