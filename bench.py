@@ -96,6 +96,7 @@ OTHER_CONFIGS = {
     "indexer_rows": ("indexer_rows", "topk", 32),
     "indexer_long": ("indexer_long", "topk", 128),
     "indexer_near_uniform": ("indexer_near_uniform", "topk", 900),
+    "decode_topp_only_nok": ("decode_topp_only", "sample_nok", 16),
     "decode_rejection": ("decode", "rejection", 16),
     "decode_topp_only_rejection": ("decode_topp_only", "rejection", 16),
 }
@@ -128,7 +129,7 @@ def other_config(name, args):
                                                          t.data_ptr(), None, s.data_ptr(), 32, tok.data_ptr(),
                                                          rnd.data_ptr(), st.data_ptr(), h)
         cname = "ts_sample_rows_rejection"
-    elif op in ("sample", "sample_logp"):
+    elif op in ("sample", "sample_logp", "sample_nok"):
         p = torch.from_numpy(b.p).to(dev)
         t = torch.from_numpy(b.t).to(dev)
         seeds = b.seeds if b.seeds is not None else wl.heavy_launch_seeds(0, rows)
@@ -140,6 +141,9 @@ def other_config(name, args):
                  ws.data_ptr(), ws.numel())
         call = lambda x, h: lib.ts_sample_rows(x, rows, vocab, vocab, *fixed, h)
         cname = "ts_sample_rows"
+        if op == "sample_nok":   # no top-k array: top-k off for every row (the nucleus pass)
+            call = lambda x, h: lib.ts_sample_rows(x, rows, vocab, vocab, None, *fixed[1:], h)
+            cname = "ts_sample_rows (top_k NULL)"
         if op == "sample_logp":
             lp = torch.empty(rows, dtype=torch.float32, device=dev)
             ls = torch.empty(rows, dtype=torch.float32, device=dev)

@@ -61,7 +61,7 @@ using namespace tsd;
 namespace {
 
 enum Mode : int { kModeTopk = 0, kModeTopp = 1, kModeSample = 2 };
-enum Path : int { kPathNone = 0, kPathCand = 1, kPathGreedy = 2, kPathFull = 3, kPathStream = 4 };
+enum Path : int { kPathNone = 0, kPathCand = 1, kPathGreedy = 2, kPathFull = 3, kPathStream = 4, kPathNucleus = 5 };
 
 // stream kernel
 constexpr int kT1 = 256;                            // threads per chunk workgroup
@@ -104,11 +104,26 @@ struct WaveInfo {
   uint32_t kmax_idx;  // lowest id holding kmax (GREEDY)
   float best_s;       // FULL sampling: best score relative to kmax's value
   int32_t best_idx;
-  uint32_t pad;
+  uint32_t kmin;      // NUCLEUS rows: smallest key among the wave's elements
 };
 static_assert(sizeof(WaveInfo) == 32, "WaveInfo layout");
 constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row state of the nucleus passes. Histograms over the first radix digit of the row's
+// keys (the bits below the common prefix of its smallest and largest key): token counts,
+// counts of tokens min-p keeps, exact fixed-point masses. Then the best Gumbel score of the
+// kept tokens above the cut bin, as (ordered score << 32 | ~id) so that the maximum prefers
+// the lowest id on equal scores, and the number of cut-bin tokens listed (the list itself
+// lives in the row's candidate slices, which nucleus rows leave unused).
+struct NucRow {
+  uint32_t cnt[kDBins];
+  uint32_t cok[kDBins];
+  uint64_t mass[kDBins];
+  uint64_t best;
+  uint32_t nlist;
+  uint32_t pad;
+};
 
 struct Params {
   const float* x;
@@ -130,6 +145,8 @@ struct Params {
   int32_t xcd_map;
   int32_t force_exact;
   int32_t direct;              // rows of <= kLdsCand logits: the row kernel alone, row in LDS
+  int32_t nucleus;             // top-k off for every row: the nucleus pass spreads top-p work
+  struct NucRow* nuc;          // per row: the nucleus pass's histograms
   int32_t* out_idx;
   int32_t* out_kept;
   uint8_t* out_mask;
@@ -205,6 +222,7 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int mode, int r) {
   else if (rp.t == 0.0f) rp.path = kPathGreedy;
   else if (rp.k_eff <= kFastK) rp.path = kPathCand;
   else if (rp.k_eff == P.V && rp.p == 1.0f && rp.minp == 0.0f) rp.path = kPathFull;
+  else if (P.nucleus && rp.k_eff == P.V) rp.path = kPathNucleus;
   else rp.path = kPathStream;
   return rp;
 }
@@ -1204,6 +1222,24 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   if (MODE == kModeTopp && P.out_mask) {
     fill_bytes_nt<kT1>(P.out_mask + (int64_t)r * P.V + c0, n, (path == kPathFull) ? (uint8_t)1 : (uint8_t)0);
   }
+  uint32_t kmin_w = 0xFFFFFFFFu;
+  if (path == kPathNucleus) {
+    // the wave's smallest key (the nucleus pass bins keys below the row's common prefix) and
+    // this workgroup's share of zeroing the row's nucleus histograms
+    float fmn = INFINITY;
+#pragma unroll
+    for (int s = 0; s < kS1; ++s) {
+      const int nv = nvalid(s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < nv) fmn = fminf(fmn, xval(s, e));
+    }
+    kmin_w = wave_min(f2key(fmn));
+    uint4* z = reinterpret_cast<uint4*>(P.nuc + r);
+    const int nz = (int)(sizeof(NucRow) / sizeof(uint4));
+    const int per = (nz + P.chunks - 1) / P.chunks;
+    for (int i = c * per + (int)threadIdx.x; i < min(nz, (c + 1) * per); i += kT1) z[i] = make_uint4(0, 0, 0, 0);
+  }
   if (l == 0) {
     WaveInfo wi;
     wi.count = count;
@@ -1213,7 +1249,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     wi.kmax_idx = kmax_idx;
     wi.best_s = best_s;
     wi.best_idx = best_idx;
-    wi.pad = 0;
+    wi.kmin = kmin_w;
     P.info[seg] = wi;
   }
 }
@@ -1376,60 +1412,66 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
   }
 }
 
+// Visits a row in global memory, f(key, id) for each of its first V elements (ids rising
+// along a thread's calls): 8 float4 loads per thread per round with the next round in flight
+// when the row is 16-byte aligned, else 16 scalar loads per thread per round.
+template <class F>
+__device__ __forceinline__ void visit_row(const float* row, uint32_t V, F f) {
+  const bool al4 = ((uintptr_t)row & 15u) == 0;
+  if (al4) {   // 8 float4 loads per thread per round; the next round loads during this one
+    const uint32_t nq = V >> 2;
+    const uint4* rq = reinterpret_cast<const uint4*>(row);
+    uint4 v[8], nx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t q = u * kRT + threadIdx.x;
+      v[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
+    }
+    for (uint32_t base = 0; base < nq; base += kRT * 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = base + kRT * 8 + u * kRT + threadIdx.x;
+        nx[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = base + u * kRT + threadIdx.x;
+        if (q < nq) {
+          f(f2key(__uint_as_float(v[u].x)), 4 * q);
+          f(f2key(__uint_as_float(v[u].y)), 4 * q + 1);
+          f(f2key(__uint_as_float(v[u].z)), 4 * q + 2);
+          f(f2key(__uint_as_float(v[u].w)), 4 * q + 3);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = nx[u];
+    }
+    for (uint32_t i = 4 * nq + threadIdx.x; i < V; i += kRT) f(f2key(row[i]), i);
+  } else {
+    for (uint32_t base = 0; base < V; base += kRT * 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t j = base + u * kRT + threadIdx.x;
+        v[u] = 0;
+        if (j < V) v[u] = f2key(row[j]);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t j = base + u * kRT + threadIdx.x;
+        if (j < V) f(v[u], j);
+      }
+    }
+  }
+}
+
 template <int MODE>
 __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
                                            uint32_t kmin, uint64_t seed, Smem& sm, double lse) {
   // The exact path over the raw row in global memory, one read of the row per pass.
   const float* row = P.x + (int64_t)r * P.stride;
   const uint32_t V = (uint32_t)rp.n;   // the row's valid length
-  const bool al4 = ((uintptr_t)row & 15u) == 0;
-  auto rvis = [&](auto f) {
-    if (al4) {   // 8 float4 loads per thread per round; the next round loads during this one
-      const uint32_t nq = V >> 2;
-      const uint4* rq = reinterpret_cast<const uint4*>(row);
-      uint4 v[8], nx[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t q = u * kRT + threadIdx.x;
-        v[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
-      }
-      for (uint32_t base = 0; base < nq; base += kRT * 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t q = base + kRT * 8 + u * kRT + threadIdx.x;
-          nx[u] = q < nq ? rq[q] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t q = base + u * kRT + threadIdx.x;
-          if (q < nq) {
-            f(f2key(__uint_as_float(v[u].x)), 4 * q);
-            f(f2key(__uint_as_float(v[u].y)), 4 * q + 1);
-            f(f2key(__uint_as_float(v[u].z)), 4 * q + 2);
-            f(f2key(__uint_as_float(v[u].w)), 4 * q + 3);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = nx[u];
-      }
-      for (uint32_t i = 4 * nq + threadIdx.x; i < V; i += kRT) f(f2key(row[i]), i);
-    } else {
-      for (uint32_t base = 0; base < V; base += kRT * 16) {
-        uint32_t v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const uint32_t j = base + u * kRT + threadIdx.x;
-          v[u] = 0;
-          if (j < V) v[u] = f2key(row[j]);
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const uint32_t j = base + u * kRT + threadIdx.x;
-          if (j < V) f(v[u], j);
-        }
-      }
-    }
-  };
+  auto rvis = [&](auto f) { visit_row(row, V, f); };
   const uint32_t ke = (uint32_t)rp.k_eff;
   Sel sk = sel_all();
   if (ke < V) sk = select_topk(rvis, ke, V, kmax, kmin, 0u, V - 1, sm);
@@ -1726,6 +1768,404 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
   return nf;
 }
 
+// ------------------------------------------------------------------ nucleus pass
+// Rows with top-k off and top-p or min-p on (NUCLEUS): rows x chunks workgroups, run after
+// the stream kernel. Each weighs its chunk against the row maximum (the same fixed-point
+// masses as the exact top-p select: S = 63 - bitlen(V)), bins the keys by the first radix
+// digit below the row's common key prefix, and adds per bin the token count, the count min-p
+// keeps, the mass and - when sampling - the best Gumbel score of the kept tokens into the
+// row's NucRow. The row kernel then needs only the bin where the nucleus ends.
+// f(x, i) for the n elements of a chunk starting at `row` (NT threads; float4 loads, four
+// per thread in flight, when the chunk is 16-byte aligned).
+template <int NT, class F>
+__device__ __forceinline__ void chunk_visit(const float* row, int n, F f) {
+  if (((uintptr_t)row & 15u) == 0) {
+    const int nq = n >> 2;
+    const float4* rq = reinterpret_cast<const float4*>(row);
+    for (int q0 = threadIdx.x; q0 < nq; q0 += 4 * NT) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * NT;
+        v[u] = q < nq ? rq[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * NT;
+        if (q < nq) {
+          f(v[u].x, (uint32_t)(4 * q));
+          f(v[u].y, (uint32_t)(4 * q + 1));
+          f(v[u].z, (uint32_t)(4 * q + 2));
+          f(v[u].w, (uint32_t)(4 * q + 3));
+        }
+      }
+    }
+    for (int i = 4 * nq + (int)threadIdx.x; i < n; i += NT) f(row[i], (uint32_t)i);
+  } else {
+    for (int i = threadIdx.x; i < n; i += NT) f(row[i], (uint32_t)i);
+  }
+}
+
+struct SmemN {
+  uint32_t cnt[kDBins];
+  uint32_t cok[kDBins];
+  uint64_t mass[kDBins];
+  uint32_t red[4 * kW1];
+};
+
+// The row plan and key range of a NUCLEUS row from its wave summaries (common to the nucleus
+// kernels). Returns false for rows that are not NUCLEUS or that the row kernel rejects.
+struct NucPlan {
+  RowPlan rp;
+  uint32_t kmax, kmin;
+};
+template <int MODE, int NT, int NW>
+__device__ __forceinline__ bool nucleus_plan(const Params& P, int r, uint32_t* red, NucPlan& np) {
+  np.rp = plan_row(P, MODE, r);
+  if (np.rp.path != kPathNucleus) return false;        // uniform
+  const int nseg = P.chunks * kW1;
+  const WaveInfo* inf = P.info + (int64_t)r * nseg;
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, flags = 0, dummy = 0u;
+  for (int i = threadIdx.x; i < nseg; i += NT) {
+    const WaveInfo wi = inf[i];
+    kmax = max(kmax, wi.kmax);
+    kmin = min(kmin, wi.kmin);
+    flags |= wi.flags;
+  }
+  block_reduce4<NW>(kmax, dummy, kmin, flags, red);
+  np.kmax = kmax;
+  np.kmin = kmin;
+  return !((flags & kFlagNan) || kmax >= kKeyPosInf || kmax <= kKeyNegInf);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kT1) void ts_nucleus_kernel(Params P) {
+  __shared__ SmemN sm;
+  const int b = (int)blockIdx.x;
+  int L = b;
+  if (P.xcd_map) {
+    const int per = (P.rows * P.chunks) >> 3;
+    L = (b & 7) * per + (b >> 3);
+  }
+  const int r = L / P.chunks;
+  const int c = L - r * P.chunks;
+  NucPlan np;
+  if (!nucleus_plan<MODE, kT1, kW1>(P, r, sm.red, np)) return;   // uniform
+  const RowPlan& rp = np.rp;
+  const uint32_t kmax = np.kmax, kmin = np.kmin;
+  for (int i = threadIdx.x; i < kDBins; i += kT1) {
+    sm.cnt[i] = 0u;
+    sm.cok[i] = 0u;
+    sm.mass[i] = 0ull;
+  }
+  const float m = key2f(kmax);
+  const double c2 = kLog2e / (double)rp.t;
+  const int S = 63 - bitlen((uint32_t)P.V);
+  const Digit g = first_digit(kmax, kmin);
+  const bool minp_on = rp.minp > 0.0f;
+  const int c0 = c * P.chunk_len;
+  const int n = max(0, min(P.chunk_len, P.V - c0));
+  const float* row = P.x + (int64_t)r * P.stride + c0;
+  bar();
+  chunk_visit<kT1>(row, n, [&](float x, uint32_t) {
+    const uint32_t key = f2key(x);
+    const uint32_t bin = (key >> g.sh) & g.dm;
+    const float w = weight32(key, m, c2);
+    hist_add(sm.cnt, bin);
+    atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)mass32_of(w, S));
+    if (!minp_on || w >= rp.minp) atomicAdd(&sm.cok[bin], 1u);
+  });
+  bar();
+  NucRow* nr = P.nuc + r;
+  for (int i = threadIdx.x; i < kDBins; i += kT1) {
+    const uint32_t cn = sm.cnt[i];
+    if (cn) {
+      atomicAdd(&nr->cnt[i], cn);
+      const uint32_t co = sm.cok[i];
+      if (co) atomicAdd(&nr->cok[i], co);
+      atomicAdd((unsigned long long*)&nr->mass[i], (unsigned long long)sm.mass[i]);
+    }
+  }
+}
+
+// Second nucleus pass (rows x chunks, after the histograms are complete): every workgroup of a
+// row finds the same cut bin - the bin holding the nucleus's last token - from the row's
+// masses. Its chunk's tokens in bins above the cut are all in the nucleus: sampling draws
+// their Gumbel scores (min-p kept ones) into the row's best; top-p with a mask writes their
+// bytes. Tokens of the cut bin are appended, in any order, to the row's list for the row
+// kernel's exact cut.
+struct SmemC {
+  uint32_t red[4 * kW1];
+  uint64_t red64[2 * kW1];
+  uint32_t res[2];
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
+  __shared__ SmemC sm;
+  const int b = (int)blockIdx.x;
+  int L = b;
+  if (P.xcd_map) {
+    const int per = (P.rows * P.chunks) >> 3;
+    L = (b & 7) * per + (b >> 3);
+  }
+  const int r = L / P.chunks;
+  const int c = L - r * P.chunks;
+  NucPlan np;
+  if (!nucleus_plan<MODE, kT1, kW1>(P, r, sm.red, np)) return;
+  const RowPlan& rp = np.rp;
+  NucRow* nr = P.nuc + r;
+  const Digit g = first_digit(np.kmax, np.kmin);
+  int cut = -1;
+  if (rp.p != 1.0f) {
+    constexpr int kB = kDBins / kT1;                   // 8 bins per thread, thread t: 8t .. 8t+7
+    uint64_t ms[kB], tsum = 0;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      ms[j] = nr->mass[kB * threadIdx.x + j];
+      tsum += ms[j];
+    }
+    const uint64_t suf = wave_incl_suffix64(tsum);    // this and higher lanes of the wave
+    if (lane() == 0) sm.red64[wave()] = suf;
+    if (threadIdx.x == 0) sm.res[0] = 0xFFFFFFFFu;
+    bar();
+    uint64_t above = suf - tsum, z = 0;
+#pragma unroll
+    for (int w = 0; w < kW1; ++w) {
+      z += sm.red64[w];
+      if (w > wave()) above += sm.red64[w];
+    }
+    const uint64_t target = topp_target(rp.p, z);
+    if (above < target && above + tsum >= target) {
+      uint64_t acc = above;
+      int j = kB - 1;
+      for (; j > 0; --j) {
+        if (acc + ms[j] >= target) break;
+        acc += ms[j];
+      }
+      sm.res[0] = (uint32_t)(kB * threadIdx.x + j);
+    }
+    bar();
+    cut = (int)sm.res[0];
+  }
+  const float m = key2f(np.kmax);
+  const double c2 = kLog2e / (double)rp.t;
+  const bool minp_on = rp.minp > 0.0f;
+  const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int c0 = c * P.chunk_len;
+  const int n = max(0, min(P.chunk_len, P.V - c0));
+  const float* row = P.x + (int64_t)r * P.stride + c0;
+  uint8_t* mrow = (MODE == kModeTopp && P.out_mask) ? P.out_mask + (int64_t)r * P.V + c0 : nullptr;
+  // the chunk in registers: thread t holds quads t, t + kT1, ... (ids rise along them)
+  constexpr int kQ = kChunkMax / 4 / kT1;
+  float4 v[kQ];
+  const int nq = (n + 3) >> 2;
+  const bool al = ((uintptr_t)row & 15u) == 0;
+#pragma unroll
+  for (int s = 0; s < kQ; ++s) {
+    const int q = (int)threadIdx.x + s * kT1;
+    v[s] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (q < nq) {
+      if (al && 4 * q + 3 < n) {
+        v[s] = reinterpret_cast<const float4*>(row)[q];
+      } else {
+        v[s].x = row[4 * q];
+        v[s].y = 4 * q + 1 < n ? row[4 * q + 1] : -INFINITY;
+        v[s].z = 4 * q + 2 < n ? row[4 * q + 2] : -INFINITY;
+        v[s].w = 4 * q + 3 < n ? row[4 * q + 3] : -INFINITY;
+      }
+    }
+  }
+  auto elem = [&](int s, int e) { return e == 0 ? v[s].x : (e == 1 ? v[s].y : (e == 2 ? v[s].z : v[s].w)); };
+  auto valid = [&](int s, int e) { return 4 * ((int)threadIdx.x + s * kT1) + e < n; };
+  // cut-bin members: count (one LDS add per wave, one global reservation per workgroup)
+  uint32_t mine = 0;
+  if (cut >= 0) {
+#pragma unroll
+    for (int s = 0; s < kQ; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(s, e) && (int)((f2key(elem(s, e)) >> g.sh) & g.dm) == cut) ++mine;
+  }
+  const uint32_t wincl = wave_incl_scan(mine);
+  const uint32_t wtot = wave_total(wincl);
+  if (threadIdx.x == 0) sm.res[1] = 0u;
+  bar();
+  uint32_t wbase = 0;
+  if (lane() == 0 && wtot) wbase = atomicAdd(&sm.res[1], wtot);
+  bar();
+  if (threadIdx.x == 0 && sm.res[1]) sm.res[0] = atomicAdd(&nr->nlist, sm.res[1]);
+  bar();
+  const int nseg = P.chunks * kW1;
+  uint2* list = P.cand + (int64_t)r * nseg * P.cap_w;
+  const uint32_t cap_list = (uint32_t)min((int64_t)kLdsCand, (int64_t)nseg * P.cap_w);
+  uint32_t at = sm.res[0] + (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase) + wincl - mine;
+  uint64_t best = 0;
+#pragma unroll
+  for (int s = 0; s < kQ; ++s) {
+    const uint32_t id0 = (uint32_t)(c0 + 4 * ((int)threadIdx.x + s * kT1));
+    bool mem[4];
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = f2key(elem(s, e));
+      const int bin = (int)((key >> g.sh) & g.dm);
+      mem[e] = false;
+      if (!valid(s, e)) continue;
+      if (bin == cut) {
+        if (at < cap_list) list[at] = make_uint2(key, id0 + e);
+        ++at;
+      } else if (bin > cut) {
+        mem[e] = !minp_on || weight32(key, m, c2) >= rp.minp;
+        any |= mem[e];
+      }
+    }
+    if (MODE == kModeSample && any) {
+      const uint4 wd = philox4x32_10(id0 >> 2, (uint32_t)r, k0, k1);   // id0 is a multiple of 4
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (mem[e]) {
+          const uint32_t key = f2key(elem(s, e));
+          const float sc = (key2f(key) - m) / rp.t + gumbel_from_uniform(uniform_from_word(pick_word(wd, (uint32_t)e)));
+          best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~(id0 + e));
+        }
+      }
+    }
+    if (MODE == kModeTopp && mrow) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (mem[e]) mrow[id0 - c0 + e] = 1;
+    }
+  }
+  if (MODE == kModeSample) {
+    uint32_t hi = (uint32_t)(best >> 32);
+    hi = block_max_u32<kW1>(hi, sm.red);
+    uint32_t lo = ((uint32_t)(best >> 32) == hi) ? (uint32_t)best : 0u;
+    lo = block_max_u32<kW1>(lo, sm.red);
+    if (threadIdx.x == 0 && (hi | lo)) atomicMax((unsigned long long*)&nr->best, ((unsigned long long)hi << 32) | lo);
+  }
+}
+
+// The row kernel's side of a NUCLEUS row (both nucleus passes done): Z and the cut bin come
+// from the row's histograms exactly as the second pass found them; the cut bin's tokens come
+// from the row's list into LDS for the exact cut, the same fixed-point select as the exact
+// path. Tokens above the cut bin were handled by the second pass (their best score, their
+// mask bytes). Returns false (nothing written) when the cut bin holds more tokens than LDS:
+// the caller then runs the row-streaming path.
+template <int MODE>
+__device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
+                                               uint64_t seed, Smem& sm, double lse) {
+  const int nseg = P.chunks * kW1;
+  const WaveInfo* inf = P.info + (int64_t)r * nseg;
+  uint32_t kmin = 0xFFFFFFFFu;
+  for (int i = threadIdx.x; i < nseg; i += kRT) kmin = min(kmin, inf[i].kmin);
+  kmin = block_min_u32<kRW>(kmin, sm.red);
+  const NucRow* nr = P.nuc + r;
+  const Digit g = first_digit(kmax, kmin);
+  const uint32_t V = (uint32_t)P.V;
+  const float m = key2f(kmax);
+  const float t = rp.t;
+  const double c2 = kLog2e / (double)t;
+  const int S = 63 - bitlen(V);
+  const bool minp_on = rp.minp > 0.0f;
+  auto wmass = [&](uint32_t rk) { return mass32_of(weight32(rk, m, c2), S); };
+  auto ok = [&](uint32_t rk) { return !minp_on || weight32(rk, m, c2) >= rp.minp; };
+  // the histograms in one batch of loads: counts and masses into LDS (for the search), the
+  // kept counts in registers
+  constexpr int kPerT = kDBins / kRT;
+  uint32_t hc[kPerT], hk[kPerT];
+  uint64_t hm[kPerT];
+#pragma unroll
+  for (int j = 0; j < kPerT; ++j) {
+    const int i = (int)threadIdx.x + j * kRT;
+    hc[j] = nr->cnt[i];
+    hm[j] = nr->mass[i];
+    hk[j] = nr->cok[i];
+  }
+  uint64_t zh = 0, zl = 0;
+#pragma unroll
+  for (int j = 0; j < kPerT; ++j) {
+    const int i = (int)threadIdx.x + j * kRT;
+    sm.hist[i] = hc[j];
+    sm.mhi[i] = hm[j];
+    zh += hm[j];
+  }
+  block_sum2_u64<kRW>(zh, zl, sm.red64);
+  int cut = -1;                 // the bin holding the nucleus's last token; -1: no cut (p == 1)
+  uint32_t ncut = 0;            // tokens in the cut bin
+  Sel sp = sel_all();
+  if (rp.p != 1.0f) {
+    const uint64_t target = topp_target(rp.p, zh);
+    search_mass(sm, target, 0ull);   // reads and clears the histograms
+    cut = (int)sm.res[0];
+    const uint32_t n_above = sm.res[1];
+    ncut = sm.res[2];
+    const uint64_t ma = sm.res64[0];
+    if (ncut > (uint32_t)kLdsCand) return false;
+    const uint2* list = P.cand + (int64_t)r * nseg * P.cap_w;   // ncut entries, any order
+    for (uint32_t i0 = threadIdx.x; i0 < ncut; i0 += 8 * kRT) {
+      uint2 e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + u * kRT;
+        e[u] = i < ncut ? list[i] : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + u * kRT;
+        if (i < ncut) {
+          sm.ckey[i] = e[u].x;
+          sm.cidx[i] = e[u].y;
+        }
+      }
+    }
+    bar();
+    const uint32_t bprefix = (g.prefix << (g.lo - g.sh)) | (uint32_t)cut;   // key >> g.sh of the bin
+    const uint32_t base_key = bprefix << g.sh;
+    const uint32_t top_key = g.sh == 0 ? base_key : (base_key | ((1u << g.sh) - 1u));
+    uint32_t kept_unused;
+    sp = select_mass<false>(LdsVis{sm.ckey, sm.cidx, ncut}, wmass, target, ncut, top_key, base_key, 0u, V - 1,
+                            sm, kept_unused, false, ma, n_above);
+  }
+  if (MODE == kModeTopp) {
+    // kept: tokens of bins above the cut that min-p keeps, plus the cut bin's kept members
+    uint64_t c = 0, z = 0;
+#pragma unroll
+    for (int j = 0; j < kPerT; ++j)
+      if ((int)threadIdx.x + j * kRT > cut) c += hk[j];
+    uint8_t* mrow = P.out_mask ? P.out_mask + (int64_t)r * P.V : nullptr;
+    for (uint32_t i = threadIdx.x; i < ncut; i += kRT) {
+      if (sel_member(sp, sm.ckey[i], sm.cidx[i]) && ok(sm.ckey[i])) {
+        c += 1;
+        if (mrow) mrow[sm.cidx[i]] = 1;
+      }
+    }
+    block_sum2_u64<kRW>(c, z, sm.red64);
+    if (threadIdx.x == 0) P.out_kept[r] = (int32_t)c;
+  } else if (MODE == kModeSample) {
+    uint64_t best = threadIdx.x == 0 ? nr->best : 0ull;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    for (uint32_t i = threadIdx.x; i < ncut; i += kRT) {
+      const uint32_t key = sm.ckey[i], id = sm.cidx[i];
+      if (sel_member(sp, key, id) && ok(key)) {
+        const float sc = gumbel_score(key, id, m, t, (uint32_t)r, k0, k1);
+        best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~id);
+      }
+    }
+    uint32_t hi = (uint32_t)(best >> 32);
+    hi = block_max_u32<kRW>(hi, sm.red);
+    uint32_t lo = ((uint32_t)(best >> 32) == hi) ? (uint32_t)best : 0u;
+    lo = block_max_u32<kRW>(lo, sm.red);
+    const int32_t tok = (int32_t)~lo;
+    if (threadIdx.x == 0) {
+      P.out_token[r] = tok;
+      put_logp(P, r, tok, t, lse);
+    }
+  }
+  return true;
+}
+
 // Top-k select output of a certified candidate selection: the selected ids ascending (or in
 // the row ordering for TS_ORDER_VALUE), shifted by the row's offset, then -1 padding.
 __device__ __forceinline__ void emit_topk_cand(const Params& P, const RowPlan& rp, int r, uint32_t ntot,
@@ -1911,6 +2351,8 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     }
     return;
   }
+
+  if (path == kPathNucleus && nucleus_finish<MODE>(P, rp, r, kmax, seed, sm, lse)) return;
 
   // the smallest key the exact path must consider (a lower bound of the row's k-th key)
   uint32_t kfloor = kKeyNegInf;
@@ -2131,7 +2573,7 @@ std::atomic<int64_t> g_knob_direct{1};
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
-  size_t off_info = 0, off_cand = 0, off_wsum = 0, total = 0;
+  size_t off_info = 0, off_cand = 0, off_wsum = 0, off_nuc = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -2160,6 +2602,8 @@ bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   b += align256(nseg * (size_t)pl.cap_w * sizeof(uint2));
   pl.off_wsum = b;
   b += align256(nseg * sizeof(double));
+  pl.off_nuc = b;
+  b += align256((size_t)rr * sizeof(NucRow));
   pl.total = b;
   return true;
 }
@@ -2208,6 +2652,9 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.force_exact = (int32_t)g_knob_exact.load();
   // Rows that fit the row kernel's LDS skip the stream kernel (unless a chunk size is forced).
   P.direct = (V <= kLdsCand && g_knob_chunk.load() == 0 && g_knob_direct.load() != 0) ? 1 : 0;
+  // No top-k array: every row has top-k off, so rows with top-p or min-p on take the
+  // nucleus pass (spread over the chunk workgroups) instead of one workgroup streaming the row.
+  P.nucleus = (MODE != kModeTopk && !P.direct && !P.force_exact && k == nullptr && (p != nullptr || minp != nullptr)) ? 1 : 0;
   P.out_idx = out_idx;
   P.out_kept = out_kept;
   P.out_mask = out_mask;
@@ -2219,12 +2666,21 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.info = reinterpret_cast<WaveInfo*>(w + pl.off_info);
   P.cand = reinterpret_cast<uint2*>(w + pl.off_cand);
   P.wsum = (out_logp || out_lse) ? reinterpret_cast<double*>(w + pl.off_wsum) : nullptr;
+  P.nuc = reinterpret_cast<NucRow*>(w + pl.off_nuc);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (!P.direct) {
     hipLaunchKernelGGL(ts_stream_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "stream kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (P.nucleus) {
+    hipLaunchKernelGGL(ts_nucleus_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "nucleus kernel launch failed: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(ts_nucleus_cut_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "nucleus cut kernel launch failed: %s", hipGetErrorString(e));
   }
   hipLaunchKernelGGL(ts_row_kernel<MODE>, dim3((unsigned)rows), dim3(kRT), 0, s, P);
   e = hipGetLastError();

@@ -295,6 +295,16 @@ __device__ __forceinline__ float gumbel_from_uniform(float u) {
 // totals do not depend on the order of the additions: a weight w in [0, 1] counts as
 // floor(w * 2^S), S chosen per row so that n weights cannot overflow (S = 63 - bitlen(n)).
 __device__ __forceinline__ uint64_t mass1_of(double w, int s) { return (uint64_t)ldexp(w, s); }
+// The same floor(w * 2^s) for an fp32 weight w in [0, 1] and s <= 62, from w's bits: a normal
+// w is m24 * 2^(E - 150) (E its biased exponent); zero and subnormals (below 2^-126) give 0.
+__device__ __forceinline__ uint64_t mass32_of(float w, int s) {
+  const uint32_t b = __float_as_uint(w);
+  const int e = (int)((b >> 23) & 0xFFu);
+  if (e == 0) return 0ull;
+  const uint64_t m = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+  const int sh = e - 150 + s;
+  return sh >= 0 ? (m << sh) : (sh > -24 ? (m >> -sh) : 0ull);
+}
 
 
 // ---------------------------------------------------------------- weights
