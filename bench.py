@@ -255,10 +255,12 @@ def rejection_matrix(args):
                 k = torch.full((rows,), kk if kk else vocab, dtype=torch.int32, device=dev)
                 p = torch.full((rows,), pp, dtype=torch.float32, device=dev)
                 mp = torch.full((rows,), mm, dtype=torch.float32, device=dev)
-                exact = lambda x: lib.ts_sample_rows_minp(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                # no top-k array when the filter has no top-k (the exact sampler's nucleus passes)
+                kp = k.data_ptr() if kk else None
+                exact = lambda x: lib.ts_sample_rows_minp(x, rows, vocab, vocab, kp, p.data_ptr(),
                                                           t.data_ptr(), mp.data_ptr(), s.data_ptr(), tok.data_ptr(),
                                                           st.data_ptr(), ws.data_ptr(), ws.numel(), h)
-                rej = lambda x: lib.ts_sample_rows_rejection(x, rows, vocab, vocab, k.data_ptr(), p.data_ptr(),
+                rej = lambda x: lib.ts_sample_rows_rejection(x, rows, vocab, vocab, kp, p.data_ptr(),
                                                              t.data_ptr(), mp.data_ptr(), s.data_ptr(), 32,
                                                              tok.data_ptr(), rnd.data_ptr(), st.data_ptr(), h)
                 us_exact = timed(exact, ptrs, args.steps)

@@ -136,7 +136,11 @@ int ts_topk_select_rows(const float* keys, int64_t rows, int64_t row_len, int64_
  * temperature -> top-k -> top-p. With w_i = exp((x_i - max)/T) over the top-k set K and
  * Z = sum_K w, the kept set P is the shortest prefix of K (in the row ordering) whose
  * weight reaches p * Z (>=). P always holds the row maximum.
- *   top_k, top_p, temperature   [rows] or NULL.
+ *   top_k, top_p, temperature   [rows] or NULL. With top_k NULL (top-k off for every row)
+ *               and top_p or min_p given, rows of more than 12288 logits with top-p or
+ *               min-p on spread their work over the row's chunk workgroups (two extra
+ *               launches: mass histograms, then the cut bin); the results are the same
+ *               bytes as with a top_k array of k >= vocab, which keeps one workgroup per row.
  *   out_kept    [rows] int32: |P|.
  *   out_mask    [rows, vocab] uint8 or NULL: 1 for tokens in P, else 0 (dense, row pitch
  *               = vocab bytes).
