@@ -189,7 +189,7 @@ struct Weigh {
   __device__ __forceinline__ uint64_t mass(uint32_t key, bool& ok) const {
     const float w = weight32(key, m, c2);
     ok = !(minp > 0.0f) || w >= minp;
-    return mass1_of((double)w, S);
+    return mass64_of(w, S);
   }
 };
 

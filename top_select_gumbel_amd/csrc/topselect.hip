@@ -1325,7 +1325,7 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
     // (S = 63 - bitlen(|K|); truncation costs < |K| * 2^-S of Z >= 1).
     const int S = 63 - bitlen(nk);
     const double c2 = kLog2e / (double)t;
-    auto wmass = [&](uint32_t rk) { return mass1_of((double)weight32(rk, m, c2), S); };
+    auto wmass = [&](uint32_t rk) { return mass32_of(weight32(rk, m, c2), S); };
     const Digit g = first_digit(kmax, klo);
     const bool pre = g.lo > 0;
     // When sampling, the same visit draws every item's Gumbel score into gsc[i] (the
@@ -1517,7 +1517,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
     // digit over [klo, kmax], where every key of K lies).
     const int S = 63 - bitlen(ke);
     const double c2 = kLog2e / (double)t;
-    auto wmass = [&](uint32_t rk) { return mass1_of((double)weight32(rk, m, c2), S); };
+    auto wmass = [&](uint32_t rk) { return mass32_of(weight32(rk, m, c2), S); };
     const uint32_t klo = (sk.lo >= 32) ? kmin : max(kmin, shl(sk.prefix, sk.lo));
     const Digit g = first_digit(kmax, klo);
     const bool pre = g.lo > 0;

@@ -294,9 +294,12 @@ __device__ __forceinline__ float gumbel_from_uniform(float u) {
 // Probability mass is summed exactly in unsigned 64-bit fixed point so that histograms and
 // totals do not depend on the order of the additions: a weight w in [0, 1] counts as
 // floor(w * 2^S), S chosen per row so that n weights cannot overflow (S = 63 - bitlen(n)).
-__device__ __forceinline__ uint64_t mass1_of(double w, int s) { return (uint64_t)ldexp(w, s); }
-// The same floor(w * 2^s) for an fp32 weight w in [0, 1] and s <= 62, from w's bits: a normal
-// w is m24 * 2^(E - 150) (E its biased exponent); zero and subnormals (below 2^-126) give 0.
+// Computed from the fp32 weight's bits (s <= 62): a normal w is m24 * 2^(E - 150) (E its
+// biased exponent), so the product is a shift of m24; zero and subnormals (below 2^-126)
+// give 0. Equal to (uint64_t)ldexp((double)w, s) for every such w.
+// The same value through binary64 (exact: a power-of-two scale, then truncation). Measured
+// faster than the shifts in the rejection kernel's all-token passes, slower elsewhere.
+__device__ __forceinline__ uint64_t mass64_of(float w, int s) { return (uint64_t)ldexp((double)w, s); }
 __device__ __forceinline__ uint64_t mass32_of(float w, int s) {
   const uint32_t b = __float_as_uint(w);
   const int e = (int)((b >> 23) & 0xFFu);
