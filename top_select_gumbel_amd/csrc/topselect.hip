@@ -1806,11 +1806,12 @@ __device__ __forceinline__ void chunk_visit(const float* row, int n, F f) {
   }
 }
 
+constexpr int kNT = 512;   // threads of the histogram pass (its LDS allows 4 workgroups per CU)
 struct SmemN {
   uint32_t cnt[kDBins];
   uint32_t cok[kDBins];
   uint64_t mass[kDBins];
-  uint32_t red[4 * kW1];
+  uint32_t red[4 * (kNT / 64)];
 };
 
 // The row plan and key range of a NUCLEUS row from its wave summaries (common to the nucleus
@@ -1839,7 +1840,7 @@ __device__ __forceinline__ bool nucleus_plan(const Params& P, int r, uint32_t* r
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kT1) void ts_nucleus_kernel(Params P) {
+__global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   __shared__ SmemN sm;
   const int b = (int)blockIdx.x;
   int L = b;
@@ -1850,10 +1851,10 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_kernel(Params P) {
   const int r = L / P.chunks;
   const int c = L - r * P.chunks;
   NucPlan np;
-  if (!nucleus_plan<MODE, kT1, kW1>(P, r, sm.red, np)) return;   // uniform
+  if (!nucleus_plan<MODE, kNT, kNT / 64>(P, r, sm.red, np)) return;   // uniform
   const RowPlan& rp = np.rp;
   const uint32_t kmax = np.kmax, kmin = np.kmin;
-  for (int i = threadIdx.x; i < kDBins; i += kT1) {
+  for (int i = threadIdx.x; i < kDBins; i += kNT) {
     sm.cnt[i] = 0u;
     sm.cok[i] = 0u;
     sm.mass[i] = 0ull;
@@ -1867,7 +1868,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_kernel(Params P) {
   const int n = max(0, min(P.chunk_len, P.V - c0));
   const float* row = P.x + (int64_t)r * P.stride + c0;
   bar();
-  chunk_visit<kT1>(row, n, [&](float x, uint32_t) {
+  chunk_visit<kNT>(row, n, [&](float x, uint32_t) {
     const uint32_t key = f2key(x);
     const uint32_t bin = (key >> g.sh) & g.dm;
     const float w = weight32(key, m, c2);
@@ -1877,7 +1878,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_kernel(Params P) {
   });
   bar();
   NucRow* nr = P.nuc + r;
-  for (int i = threadIdx.x; i < kDBins; i += kT1) {
+  for (int i = threadIdx.x; i < kDBins; i += kNT) {
     const uint32_t cn = sm.cnt[i];
     if (cn) {
       atomicAdd(&nr->cnt[i], cn);
@@ -1898,6 +1899,8 @@ struct SmemC {
   uint32_t red[4 * kW1];
   uint64_t red64[2 * kW1];
   uint32_t res[2];
+  uint32_t mkey[kW1][256];     // a wave's members of one load slot (compacted for the noise)
+  uint32_t mid[kW1][256];
 };
 
 template <int MODE>
@@ -2002,11 +2005,11 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   const uint32_t cap_list = (uint32_t)min((int64_t)kLdsCand, (int64_t)nseg * P.cap_w);
   uint32_t at = sm.res[0] + (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase) + wincl - mine;
   uint64_t best = 0;
+  const int w = wave(), l = lane();
 #pragma unroll
   for (int s = 0; s < kQ; ++s) {
     const uint32_t id0 = (uint32_t)(c0 + 4 * ((int)threadIdx.x + s * kT1));
     bool mem[4];
-    bool any = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t key = f2key(elem(s, e));
@@ -2018,18 +2021,31 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
         ++at;
       } else if (bin > cut) {
         mem[e] = !minp_on || weight32(key, m, c2) >= rp.minp;
-        any |= mem[e];
       }
     }
-    if (MODE == kModeSample && any) {
-      const uint4 wd = philox4x32_10(id0 >> 2, (uint32_t)r, k0, k1);   // id0 is a multiple of 4
+    if (MODE == kModeSample) {
+      // members are scattered over the wave's lanes: compact them first, so that the
+      // generator and the noise run on full lanes (once per member, not once per quad of
+      // every lane whenever any lane has one)
+      uint32_t nmem = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const uint64_t bal = __ballot(mem[e]);
         if (mem[e]) {
-          const uint32_t key = f2key(elem(s, e));
-          const float sc = (key2f(key) - m) / rp.t + gumbel_from_uniform(uniform_from_word(pick_word(wd, (uint32_t)e)));
-          best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~(id0 + e));
+          const uint32_t pos = nmem + mbcnt(bal);
+          sm.mkey[w][pos] = f2key(elem(s, e));
+          sm.mid[w][pos] = id0 + (uint32_t)e;
         }
+        nmem += (uint32_t)__popcll(bal);
+      }
+      if (nmem) {
+        wave_lds_sync();
+        for (uint32_t j = (uint32_t)l; j < nmem; j += 64) {
+          const uint32_t key = sm.mkey[w][j], id = sm.mid[w][j];
+          const float sc = gumbel_score(key, id, m, rp.t, (uint32_t)r, k0, k1);
+          best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~id);
+        }
+        wave_lds_sync();
       }
     }
     if (MODE == kModeTopp && mrow) {
@@ -2675,7 +2691,7 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
     if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "stream kernel launch failed: %s", hipGetErrorString(e));
   }
   if (P.nucleus) {
-    hipLaunchKernelGGL(ts_nucleus_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
+    hipLaunchKernelGGL(ts_nucleus_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kNT), 0, s, P);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "nucleus kernel launch failed: %s", hipGetErrorString(e));
     hipLaunchKernelGGL(ts_nucleus_cut_kernel<MODE>, dim3((unsigned)(rows * pl.chunks)), dim3(kT1), 0, s, P);
