@@ -196,6 +196,8 @@ struct Smem {
 struct Smem1 {
   uint32_t hist[kHWords];      // sample keys by their top 11 bits
   uint32_t hist2[kH2Bins];     // sample keys inside the chosen bin, by their next 8 bits
+  alignas(16) uint32_t hwin[kH2Bins];   // sample keys in the 256 top-16-bit bins below the maximum
+  uint32_t wmax[kW1];          // per wave: the sample's largest key
   uint4 stage_v[kW1][kQStage];
   uint32_t stage_q[kW1][kQStage];
   uint32_t res[4];
@@ -822,14 +824,13 @@ __device__ __forceinline__ void search_hist(const uint32_t* hist, uint32_t thr, 
   constexpr int kG = 8;   // 8 groups of 4 bins per lane
   const int l = lane();
   const uint4* h4 = reinterpret_cast<const uint4*>(hist) + 9 * l;
-  uint32_t g[kG];
-  uint4 gv[kG];
+  // only the lane sums stay live (the chunk's data occupies most registers); the one lane
+  // that holds the bin reads its 32 bins again
   uint32_t lsum = 0;
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
-    gv[i] = h4[i];
-    g[i] = gv[i].x + gv[i].y + gv[i].z + gv[i].w;
-    lsum += g[i];
+    const uint4 v = h4[i];
+    lsum += v.x + v.y + v.z + v.w;
   }
   const uint32_t excl = wave_incl_suffix(lsum) - lsum;
   const uint64_t bal = __ballot(excl + lsum >= thr);
@@ -840,7 +841,8 @@ __device__ __forceinline__ void search_hist(const uint32_t* hist, uint32_t thr, 
     bool done = false;
 #pragma unroll
     for (int i = kG - 1; i >= 0; --i) {
-      const uint32_t c[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+      const uint4 v = h4[i];
+      const uint32_t c[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 3; j >= 0; --j) {
         if (!done && acc + c[j] >= thr) { bin = 4 * i + j; done = true; }
@@ -977,18 +979,38 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   // The threshold is located in two levels: a 2048-bin histogram of the top 11 key bits, then
   // a 256-bin one of the next 8 bits of the sample keys inside the chosen bin, so it sits
   // within 2^13 key units (a relative 2^-10 of the value) of the sample's j-th largest key.
+  // A sample element's key, recomputed at each use: the empty asm hides the value from
+  // common-subexpression elimination, which would otherwise keep eight keys live across the
+  // barriers (the chunk's 32 data registers leave no room for them).
+  auto skey = [&](int s, int e) -> uint32_t {
+    float xv = xval(s, e);
+    asm volatile("" : "+v"(xv));
+    return f2key(xv);
+  };
   uint32_t thr = kKeyNegInf;   // reported: every valid non-NaN element with key >= thr is emitted
   float thr_f = -INFINITY;
   if (cand) {
     for (int i = threadIdx.x; i < kHWords / 4; i += kT1) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
-    if (threadIdx.x < kH2Bins) sm.hist2[threadIdx.x] = 0u;
+    if (threadIdx.x < kH2Bins) {
+      sm.hist2[threadIdx.x] = 0u;
+      sm.hwin[threadIdx.x] = 0u;
+    }
     bar();   // LDS only: the loads above stay in flight
+    {
+      // the sample's largest value (fmaxf passes over NaN), one word per wave
+      float smx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kSampleSlots; ++s) {
-      const int nv = nvalid(s);
+      for (int s = 0; s < kSampleSlots; ++s) {
+        const int nv = nvalid(s);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < nv) atomicAdd(&sm.hist[hword(f2key(xval(s, e)) >> (32 - kHBits))], 1u);
+        for (int e = 0; e < 4; ++e) {
+          float xv = xval(s, e);
+          asm volatile("" : "+v"(xv));
+          if (e < nv) smx = fmaxf(smx, xv);
+        }
+      }
+      const uint32_t wmx = wave_max(f2key(smx));
+      if (l == 0) sm.wmax[w] = wmx;
     }
     uint32_t ns = 0;   // valid sample elements of the workgroup
 #pragma unroll
@@ -1000,33 +1022,86 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     const float mu = (float)rp.k_eff * (float)ns / (float)P.V;
     const uint32_t jt = (uint32_t)ceilf(mu + 5.0f * sqrtf(mu) + 5.0f);
     if (jt < ns) {
-      bar();   // sample histogram complete
-      if (w == 0) search_hist(sm.hist, jt, sm);
+      // Window histogram: 256 bins of 2^16 keys (aligned to the key's top 16 bits) reaching
+      // down from the sample maximum's bin, about two binades. When the sample's jt-th
+      // largest key lies inside, one pass and one search locate it, and only the sample keys
+      // near the top touch LDS. Otherwise the two-level search over the whole key range
+      // below runs instead.
       bar();
-      const uint32_t b1 = sm.res[0];
-      const uint32_t need2 = jt - sm.res[1];   // >= 1
+      const uint32_t kmw = max(max(sm.wmax[0], sm.wmax[1]), max(sm.wmax[2], sm.wmax[3])) >> 16;
 #pragma unroll
       for (int s = 0; s < kSampleSlots; ++s) {
         const int nv = nvalid(s);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t key = f2key(xval(s, e));   // recomputed: cheaper than 8 live registers
-          if (e < nv && (key >> (32 - kHBits)) == b1)
-            atomicAdd(&sm.hist2[(key >> (32 - kHBits - kH2Bits)) & (kH2Bins - 1)], 1u);
+          const uint32_t d = kmw - (skey(s, e) >> 16);   // NaN keys above the maximum wrap high
+          if (e < nv && d < (uint32_t)kH2Bins) atomicAdd(&sm.hwin[d], 1u);
         }
       }
       bar();
-      if (w == 0) search_hist2(sm.hist2, need2, sm);
-      bar();
-      uint32_t tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - kHBits - kH2Bits));
-      uint32_t in_bin = sm.res[2], need = need2 - sm.res[1];
-      // Narrow value ranges (a near-uniform row puts every sampled key in one 2^13-key bin):
-      // refine through the remaining 13 key bits, 8 then 5 at a time, while the chosen bin
-      // still holds more than kRefine sampled keys. Never taken on spread-out rows.
+      // every wave searches the 256 bins itself (four per lane, bin 0 = the top), so no
+      // barrier follows: the first bin where the running count from the top reaches jt
+      const uint4 hv = reinterpret_cast<const uint4*>(sm.hwin)[l];
+      const uint32_t c4[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t lsum = hv.x + hv.y + hv.z + hv.w;
+      const uint32_t incl = wave_incl_scan(lsum);
+      const uint64_t hit = __ballot(incl >= jt);
+      uint32_t tk = 0, in_bin = 0, need = 0;
+      int rem = 0;
+      if (hit) {
+        const int L = (int)__builtin_ctzll(hit);
+        uint32_t acc = incl - lsum, jb = 3;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          if (jb == 3u && acc + c4[j] >= jt) jb = (uint32_t)j;
+          if (jb == 3u) acc += c4[j];
+        }
+        const uint32_t b = 4u * (uint32_t)L + (uint32_t)__builtin_amdgcn_readlane((int)jb, L);
+        const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
+        tk = (kmw - b) << 16;
+        in_bin = (uint32_t)__builtin_amdgcn_readlane((int)(jb == 0 ? c4[0] : jb == 1 ? c4[1] : jb == 2 ? c4[2] : c4[3]), L);
+        need = jt - above;   // >= 1
+        rem = 16;
+      } else {
+        // the jt-th largest lies below the window: 2048 bins of the top 11 key bits, then
+        // 256 of the next 8 inside the chosen bin
+#pragma unroll
+        for (int s = 0; s < kSampleSlots; ++s) {
+          const int nv = nvalid(s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) atomicAdd(&sm.hist[hword(skey(s, e) >> (32 - kHBits))], 1u);
+        }
+        bar();   // sample histogram complete
+        if (w == 0) search_hist(sm.hist, jt, sm);
+        bar();
+        const uint32_t b1 = sm.res[0];
+        const uint32_t need2 = jt - sm.res[1];   // >= 1
+#pragma unroll
+        for (int s = 0; s < kSampleSlots; ++s) {
+          const int nv = nvalid(s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = skey(s, e);
+            if (e < nv && (key >> (32 - kHBits)) == b1)
+              atomicAdd(&sm.hist2[(key >> (32 - kHBits - kH2Bits)) & (kH2Bins - 1)], 1u);
+          }
+        }
+        bar();
+        if (w == 0) search_hist2(sm.hist2, need2, sm);
+        bar();
+        tk = (b1 << (32 - kHBits)) | (sm.res[0] << (32 - kHBits - kH2Bits));
+        in_bin = sm.res[2];
+        need = need2 - sm.res[1];
+        rem = 32 - kHBits - kH2Bits;
+      }
+      // Narrow value ranges (a near-uniform row puts every sampled key in one bin): refine
+      // through the remaining key bits, at most 8 at a time, while the chosen bin still holds
+      // more than kRefine sampled keys. Never taken on spread-out rows.
 #pragma unroll 1
-      for (int lvl = 0; lvl < 2 && in_bin > (uint32_t)kRefine; ++lvl) {
-        const int sh = lvl == 0 ? 5 : 0;
-        const int bits = lvl == 0 ? 8 : 5;
+      for (int lvl = 0; lvl < 2 && in_bin > (uint32_t)kRefine && rem > 0; ++lvl) {
+        const int bits = min(kH2Bits, rem);
+        const int sh = rem - bits;
         const uint32_t pre = tk >> (sh + bits);
         if (threadIdx.x < kH2Bins) sm.hist2[threadIdx.x] = 0u;
         bar();
@@ -1035,7 +1110,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
           const int nv = nvalid(s);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t key = f2key(xval(s, e));
+            const uint32_t key = skey(s, e);
             // narrow rows put whole waves in one bin: one atomic per wave then
             if (e < nv && (key >> (sh + bits)) == pre) hist_add(sm.hist2, (key >> sh) & ((1u << bits) - 1u));
           }
@@ -1046,6 +1121,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
         tk |= sm.res[0] << sh;
         in_bin = sm.res[2];
         need -= sm.res[1];
+        rem = sh;
       }
       if (tk > kKeyNegInf) {
         thr = tk;
@@ -1191,7 +1267,9 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     // per quad).
     const float m_w = key2f(kmax);
     const uint64_t sd = P.seed[r];
-    const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
+    // the key is uniform: scalar registers keep the ten round keys out of the vector file
+    const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sd);
+    const uint32_t k1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sd >> 32));
     const float inv_t = 1.0f / rp.t;   // one rounding per row instead of a division per token
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
