@@ -909,7 +909,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   const bool aligned = ((uintptr_t)base & 15u) == 0;
   const int nq = (n + 3) >> 2;
   const int qw = (nq + kW1 - 1) / kW1;
-  const int w = wave(), l = lane();
+  // the wave index lives in a scalar register and the thread index is rebuilt from it and the
+  // lane, so that no vector register holds the thread index through the whole kernel
+  const int w = __builtin_amdgcn_readfirstlane(wave()), l = lane();
+  const int tid = (w << 6) | l;
   const int q_lo = w * qw;
   const int q_hi = min(q_lo + qw, nq);
   const int nfull = n >> 2;
@@ -990,10 +993,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   uint32_t thr = kKeyNegInf;   // reported: every valid non-NaN element with key >= thr is emitted
   float thr_f = -INFINITY;
   if (cand) {
-    for (int i = threadIdx.x; i < kHWords / 4; i += kT1) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
-    if (threadIdx.x < kH2Bins) {
-      sm.hist2[threadIdx.x] = 0u;
-      sm.hwin[threadIdx.x] = 0u;
+    for (int i = tid; i < kHWords / 4; i += kT1) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
+    if (tid < kH2Bins) {
+      sm.hist2[tid] = 0u;
+      sm.hwin[tid] = 0u;
     }
     bar();   // LDS only: the loads above stay in flight
     {
@@ -1103,7 +1106,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
         const int bits = min(kH2Bits, rem);
         const int sh = rem - bits;
         const uint32_t pre = tk >> (sh + bits);
-        if (threadIdx.x < kH2Bins) sm.hist2[threadIdx.x] = 0u;
+        if (tid < kH2Bins) sm.hist2[tid] = 0u;
         bar();
 #pragma unroll
         for (int s = 0; s < kSampleSlots; ++s) {
@@ -1316,7 +1319,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     uint4* z = reinterpret_cast<uint4*>(P.nuc + r);
     const int nz = (int)(sizeof(NucRow) / sizeof(uint4));
     const int per = (nz + P.chunks - 1) / P.chunks;
-    for (int i = c * per + (int)threadIdx.x; i < min(nz, (c + 1) * per); i += kT1) z[i] = make_uint4(0, 0, 0, 0);
+    for (int i = c * per + tid; i < min(nz, (c + 1) * per); i += kT1) z[i] = make_uint4(0, 0, 0, 0);
   }
   if (l == 0) {
     WaveInfo wi;
