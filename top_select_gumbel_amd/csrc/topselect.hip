@@ -4,10 +4,11 @@
 //
 //   ts_stream_kernel  rows x chunks workgroups of 256 threads (4 waves). Each workgroup streams
 //                     one contiguous chunk (<= 8192 logits) of one row from HBM exactly once and
-//                     keeps it in registers. A 2048-bin histogram of a quarter of the chunk (the
-//                     first two load slots of every wave) gives a threshold L_c: the lower edge
-//                     of the bin holding the sample's j-th largest key, j a safety multiple of
-//                     the chunk's share of k. Every wave then works alone (no further
+//                     keeps it in registers. A histogram of a quarter of the chunk (the first
+//                     two load slots of every wave), 256 bins reaching down from the sample
+//                     maximum, gives a threshold L_c: the lower edge of the bin holding the
+//                     sample's j-th largest key, j a safety multiple of the chunk's share of k.
+//                     Every wave then works alone (no further
 //                     barriers): it stages the float4 quads whose maximum reaches L_c, extracts
 //                     their elements >= L_c in id order and stores them as candidates in its own
 //                     slice of the workspace, with a 32-byte summary (count, L_c, maximum, NaN
@@ -979,9 +980,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   // Poisson tail below 1e-7 per workgroup for every k up to the fast path's limit).
   // Work happens on the fp32 values: a key >= threshold-key test is a float >= test against
   // the threshold's float (ordered keys are a monotone map of fp32, with -0 == +0 in both).
-  // The threshold is located in two levels: a 2048-bin histogram of the top 11 key bits, then
-  // a 256-bin one of the next 8 bits of the sample keys inside the chosen bin, so it sits
-  // within 2^13 key units (a relative 2^-10 of the value) of the sample's j-th largest key.
+  // The threshold is located in a window of 256 bins of 2^16 keys below the sample maximum
+  // (a relative 2^-7 of the value or finer), else in two levels over the whole key range: a
+  // 2048-bin histogram of the top 11 key bits, then a 256-bin one of the next 8 bits of the
+  // sample keys inside the chosen bin.
   // A sample element's key, recomputed at each use: the empty asm hides the value from
   // common-subexpression elimination, which would otherwise keep eight keys live across the
   // barriers (the chunk's 32 data registers leave no room for them).
