@@ -406,6 +406,23 @@ def main():
     torch.cuda.synchronize()
     copy_ms = float(np.median([a.elapsed_time(b) for a, b in cps]))
 
+    # A plain read of the same buffers with the stream kernel's launch shape (the library's
+    # diagnostic read kernel): the streaming ceiling the sampling call is compared against.
+    # K back-to-back reads between one event pair, like region_us_per_call.
+    acc = torch.empty(ts.read_ceiling_partials(ROWS * VOCAB), dtype=torch.float32, device=dev)
+    for i in range(20):
+        ts.ts_read_ceiling(bufs[i % ROTATE], acc)
+    torch.cuda.synchronize()
+    e_r0, e_r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_r0.record(stream)
+    for i in range(args.steps):
+        rc = lib.ts_read_ceiling(ptrs[i % ROTATE], ROWS * VOCAB, acc.data_ptr(), stream.cuda_stream)
+        if rc:
+            raise RuntimeError(ts.ts_last_error())
+    e_r1.record(stream)
+    torch.cuda.synchronize()
+    read_ms = e_r0.elapsed_time(e_r1) / args.steps
+
     # A plain read of the same buffers (torch.sum) as a practical streaming ceiling.
     rd = []
     for i in range(min(args.steps, 100)):
@@ -447,6 +464,8 @@ def main():
         "warm_kernel_us_median": float(np.median(warm_ms)) * 1e3,
         "graph_us_per_step": None if graph_ms_per_step is None else graph_ms_per_step * 1e3,
         "effective_GBps_median": BYTES_PER_CALL / (med * 1e-3) / 1e9,
+        "read_ceiling_GBps": BYTES_PER_CALL / (read_ms * 1e-3) / 1e9,
+        "frac_of_read_ceiling": read_ms / region_ms,
         "torch_sum_read_GBps": BYTES_PER_CALL / (rd_ms * 1e-3) / 1e9,
         "copy_read_write_GBps": 2 * BYTES_PER_CALL / (copy_ms * 1e-3) / 1e9,
         "source_hash": source_hash(),

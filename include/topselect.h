@@ -256,6 +256,15 @@ int ts_gumbel_noise(uint64_t seed, int32_t row, const int32_t* tokens, int64_t n
  * and g = -log(-log1p(-u)) ([GUMBEL] "implementation breakdown"), as ts_sample_rows uses them.
  */
 int ts_noise_transform(const uint32_t* words, int64_t n, float* out_u, float* out_g, void* stream);
+/*
+ * Diagnostic: a plain streaming read of the n floats at x (device, 16-byte aligned), launched
+ * with the sampling stream kernel's shape (256-thread workgroups, eight non-temporal 16-byte
+ * loads per thread, all in flight before any is used): the read bandwidth that kernel is
+ * measured against. out (device, 4 * ceil(n / 8192) floats) receives one fp32 partial sum per
+ * wave; together they sum to the n floats (the stores keep the loads). Asynchronous on
+ * `stream`; TS_ERR_INVALID_ARG for n < 0, a NULL or misaligned pointer.
+ */
+int ts_read_ceiling(const float* x, int64_t n, float* out, void* stream);
 
 /*
  * Test-only, bit-neutral path forcing (process-wide; not thread-safe). Knobs:

@@ -38,7 +38,7 @@ TS_KNOB_DIRECT = 3
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",
-    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_noise_transform", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_noise_transform", "ts_read_ceiling", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -87,6 +87,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_noise_transform.restype = c.c_int
         lib.ts_noise_transform.argtypes = [vp, i64, vp, vp, vp]
         lib.ts_gumbel_noise.restype = c.c_int
+        lib.ts_read_ceiling.argtypes = [vp, i64, vp, vp]
+        lib.ts_read_ceiling.restype = c.c_int
         lib.ts_debug_set.argtypes = [c.c_int, i64]
         lib.ts_debug_set.restype = i64
         lib.ts_status_string.argtypes = [c.c_int]
@@ -335,6 +337,25 @@ def ts_noise_transform(words):
     g = torch.empty(n, dtype=torch.float32, device=words.device)
     _check(lib.ts_noise_transform(_ptr(words), n, _ptr(u), _ptr(g), _stream()))
     return u, g
+
+
+def read_ceiling_partials(n: int) -> int:
+    """Length of the partial-sum array ts_read_ceiling writes for n floats."""
+    return 4 * ((n + 8191) // 8192)
+
+
+def ts_read_ceiling(x, out=None):
+    """Plain streaming read of a float32 device tensor (contiguous, 16-byte aligned) with the
+    stream kernel's launch shape. Returns the per-wave fp32 partial sums (`out`, allocated when
+    None: read_ceiling_partials(x.numel()) floats). A bandwidth reference."""
+    import torch
+    lib = load_library()
+    if str(x.dtype) != "torch.float32" or not x.is_contiguous():
+        raise TopSelectError("x must be a contiguous float32 tensor")
+    if out is None:
+        out = torch.empty(max(1, read_ceiling_partials(x.numel())), dtype=torch.float32, device=x.device)
+    _check(lib.ts_read_ceiling(_ptr(x), x.numel(), _ptr(out), _stream()))
+    return out
 
 
 def ts_debug_set(knob: int, value: int) -> int:

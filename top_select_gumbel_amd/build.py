@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("topselect.hip", "rejection.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("topselect.hip", "rejection.hip", "read_ceiling.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopselect.so")
 
