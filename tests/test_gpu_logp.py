@@ -3,10 +3,12 @@ against the binary64 oracle, through the C ABI.
 
 Tolerance, from the arithmetic: each exponential is an fp32 exp2 of an argument formed in
 fp32 from (x - m_w) and log2(e)/T, so its relative error is at most 2^-23 + 3 * 2^-24 * |y|
-(y the base-2 exponent); S is a mass-weighted average of those errors, below 2.5e-6 for any
-row of these sizes (and near 1e-7 in practice); the binary64 rescaling and logarithm add
-nothing visible, and the final fp32 roundings add 2^-24 relative. Hence
-|delta| <= 3e-6 + 1.2e-7 * |value| for lse and logp.
+(y the base-2 exponent; terms below 2^-126 flush to 0, under 2^-100 of a share that holds
+the maximum's 1); S is a mass-weighted average of those errors, below 2.5e-6 for any row of
+these sizes (and near 1e-7 in practice); each wave share's rescaling to the row maximum is
+fp32-accurate (about 1.5e-7 relative) and the logarithm is accurate to 1e-7 absolute, and the
+final fp32 roundings add 2^-24 relative. Hence |delta| <= 3e-6 + 1.2e-7 * |value| for lse and
+logp.
 """
 import math
 

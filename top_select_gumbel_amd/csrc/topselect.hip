@@ -1167,8 +1167,10 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   if (MODE == kModeSample && P.wsum) {
     // [LOGP] "Design: the numeric contract": the wave's share of S = sum exp((x - m) / T),
     // here relative to the wave maximum (the row kernel rescales each share to the row
-    // maximum). exp(y) = 2^(y log2 e) in fp32, four elements per fp32 partial, binary64
-    // accumulation, a fixed lane tree: the same bits for every launch of this vocabulary.
+    // maximum). exp(y) = 2^(y log2 e) in fp32 by the hardware exp2 (results below 2^-126
+    // flush to 0: the share holds the maximum's 1, so they are below its resolution), four
+    // elements per fp32 partial, binary64 accumulation, a fixed lane tree: the same bits for
+    // every launch of this vocabulary.
     double acc = 0.0;
     if (rp.bad == TS_ROW_OK && rp.t > 0.0f && kmax > kKeyNegInf && kmax < kKeyPosInf) {
       const float m_w = key2f(kmax);
@@ -1179,7 +1181,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
         float ps = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e < nv) ps += exp2f((xval(s, e) - m_w) * c2f);
+          if (e < nv) ps += __builtin_amdgcn_exp2f((xval(s, e) - m_w) * c2f);
         acc += (double)ps;
       }
     }
@@ -2302,6 +2304,8 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
   uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
+  uint32_t kw0 = kKeyNegInf;   // the maximum key of this thread's first slice
+  double ws0 = 0.0;            // and its exponential sum (sampling with logprobs)
   RowPlan rp;
   if (P.direct) {
     // The whole row is the candidate set: its keys and ids go straight to LDS (no stream
@@ -2321,9 +2325,12 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     }
   } else {
     // Aggregate the wave summaries. Their loads are issued first; the row parameters and
-    // the seed load while they are in flight. Counts go to LDS for the slice offsets.
+    // the seed load while they are in flight. Counts go to LDS for the slice offsets. With
+    // logprobs, this thread's first slice's exponential sum loads alongside.
+    if (MODE == kModeSample && P.wsum && (int)threadIdx.x < nseg) ws0 = P.wsum[(int64_t)r * nseg + threadIdx.x];
     for (int i = threadIdx.x; i < nseg; i += kRT) {
       const WaveInfo wi = inf[i];
+      if (i == (int)threadIdx.x) kw0 = wi.kmax;
       flags |= wi.flags;
       kmax = max(kmax, wi.kmax);
       thr_max = max(thr_max, wi.thr);
@@ -2356,19 +2363,24 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   if (MODE == kModeSample && P.wsum) {
     double zpart = 0.0;
     if (st == TS_ROW_OK && rp.t > 0.0f && P.direct) {
-      // the row is in LDS: S directly, exp(y) = 2^(y log2 e) in fp32, binary64 accumulation
+      // the row is in LDS: S directly, exp(y) = 2^(y log2 e) in fp32 (hardware exp2, as in
+      // the stream kernel), binary64 accumulation
       const float m_f = key2f(kmax);
       const float c2f = (float)(1.4426950408889634 / (double)rp.t);
-      for (int i = threadIdx.x; i < rp.n; i += kRT) zpart += (double)exp2f((key2f(sm.ckey[i]) - m_f) * c2f);
+      for (int i = threadIdx.x; i < rp.n; i += kRT)
+        zpart += (double)__builtin_amdgcn_exp2f((key2f(sm.ckey[i]) - m_f) * c2f);
     } else if (st == TS_ROW_OK && rp.t > 0.0f) {
-      const double m = (double)key2f(kmax);
-      for (int i = threadIdx.x; i < nseg; i += kRT) {
+      // each wave's share rescaled by exp((m_w - m) / T), fp32-accurate (the weights' form)
+      const float m_f = key2f(kmax);
+      const double c2 = kLog2e / (double)rp.t;
+      if ((int)threadIdx.x < nseg && kw0 > kKeyNegInf) zpart += ws0 * (double)weight32(kw0, m_f, c2);
+      for (int i = kRT + (int)threadIdx.x; i < nseg; i += kRT) {
         const uint32_t kw = inf[i].kmax;
-        if (kw > kKeyNegInf) zpart += P.wsum[(int64_t)r * nseg + i] * exp(((double)key2f(kw) - m) / (double)rp.t);
+        if (kw > kKeyNegInf) zpart += P.wsum[(int64_t)r * nseg + i] * (double)weight32(kw, m_f, c2);
       }
     }
     const double z = block_sum_f64<kRW>(zpart, reinterpret_cast<double*>(sm.red64));
-    lse = (double)key2f(kmax) / (double)rp.t + log(z);
+    lse = (double)key2f(kmax) / (double)rp.t + log_fast(z);
   }
 
   if (MODE == kModeTopp && P.direct && P.out_mask) {

@@ -324,6 +324,15 @@ __device__ __forceinline__ float weight32(uint32_t key, float m, double c2) {
   return ldexpf(exp2f((float)(z - n)), (int)n);
 }
 
+// Natural logarithm of a positive normal binary64 z, fp32-accurate (absolute error below
+// 1e-7 for z >= 1): z = f * 2^e with f in [0.5, 1), log z = (e + log2 f) ln 2, log2 f from the
+// hardware base-2 logarithm of fp32(f).
+__device__ __forceinline__ double log_fast(double z) {
+  int e;
+  const double f = frexp(z, &e);
+  return ((double)e + (double)__builtin_amdgcn_logf((float)f)) * 0.6931471805599453;
+}
+
 // ceil(p * Z) for p = fp32 in (0, 1) and a fixed-point total Z: with p = mant * 2^-psh
 // (mant < 2^24) the product is exact in 128 bits.
 __device__ __forceinline__ uint64_t topp_target(float p, uint64_t z) {
