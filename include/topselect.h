@@ -31,6 +31,8 @@
  *     the host inside these calls.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
  *     stream): they enqueue kernels and return; they never synchronise.
+ *   - rows == 0 (an empty batch) returns TS_OK at once once vocab and row_stride are valid:
+ *     nothing is read or written and every pointer may be NULL.
  *   - Ordering of a row: by (logit descending, token id ascending); -0.0 and +0.0 are equal.
  *     Top-k ranks the raw fp32 logits; temperature enters only exp((x - max)/T) and the
  *     Gumbel score (x - max)/T + g.

@@ -70,8 +70,15 @@ def test_bad_arguments_fail_before_any_device_work(lib):
     assert rc == ts.TS_ERR_WORKSPACE and "aligned" in lib.ts_last_error().decode()
     rc = lib.ts_sample_rows(fake, 2, 10, 10, None, None, None, fake, fake, None, fake, 16, None)
     assert rc == ts.TS_ERR_WORKSPACE and "needs" in lib.ts_last_error().decode()
-    # zero rows is a no-op that succeeds
+    # zero rows is a no-op that succeeds, with any pointers (an empty tensor's are NULL)
     assert lib.ts_sample_rows(fake, 0, 10, 10, None, None, None, None, None, None, None, 0, None) == ts.TS_OK
+    assert lib.ts_sample_rows(None, 0, 10, 10, None, None, None, None, None, None, None, 0, None) == ts.TS_OK
+    assert lib.ts_topk_select(None, 0, 10, 10, None, 4, None, None, None, 0, None) == ts.TS_OK
+    assert lib.ts_topp_mask(None, 0, 10, 10, None, None, None, None, None, None, None, 0, None) == ts.TS_OK
+    assert lib.ts_sample_rows_rejection(None, 0, 10, 10, None, None, None, None, None, 8, None, None, None,
+                                        None) == ts.TS_OK
+    # ... but not with an invalid shape
+    assert lib.ts_sample_rows(None, 0, 0, 10, None, None, None, None, None, None, None, 0, None) == ts.TS_ERR_INVALID_ARG
 
 
 def test_status_strings_and_knobs(lib):

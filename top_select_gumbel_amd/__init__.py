@@ -135,10 +135,14 @@ def ts_workspace_bytes(op: int, rows: int, vocab: int, k_max: int = 0) -> int:
 
 
 def _rows_view(x):
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2:
         raise TopSelectError("logits must be a 2-D tensor with unit column stride")
     if not x.is_cuda or x.dtype.is_complex or str(x.dtype) != "torch.float32":
         raise TopSelectError("logits must be a float32 CUDA/HIP tensor")
+    if x.shape[0] == 0:   # an empty batch: strides carry no layout (numpy gives them as 0)
+        return 0, x.shape[1], x.shape[1]
+    if x.stride(1) != 1:
+        raise TopSelectError("logits must be a 2-D tensor with unit column stride")
     return x.shape[0], x.shape[1], x.stride(0)
 
 

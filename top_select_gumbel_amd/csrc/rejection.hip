@@ -515,17 +515,17 @@ extern "C" int ts_sample_rows_rejection(const float* logits, int64_t rows, int64
                                         const float* min_p, const uint64_t* seed, int32_t max_rounds,
                                         int32_t* out_token, int32_t* out_rounds, int32_t* row_status,
                                         void* stream) {
-  if (!logits) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (vocab < 1 || vocab > TS_MAX_VOCAB)
     return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)vocab);
   if (row_stride < vocab)
     return fail(TS_ERR_INVALID_ARG, "row_stride %lld < vocab %lld", (long long)row_stride, (long long)vocab);
-  if (rows > 0x7FFFFFFF) return fail(TS_ERR_INVALID_ARG, "rows too large");
   if (max_rounds < 0 || max_rounds > kMaxRejRounds)
     return fail(TS_ERR_INVALID_ARG, "max_rounds = %d outside [0, %d]", (int)max_rounds, kMaxRejRounds);
-  if (rows > 0 && (!seed || !out_token)) return fail(TS_ERR_INVALID_ARG, "seed and out_token are required");
-  if (rows == 0) return TS_OK;
+  if (rows == 0) return TS_OK;   // an empty batch: nothing to read or write
+  if (!logits) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
+  if (rows > 0x7FFFFFFF) return fail(TS_ERR_INVALID_ARG, "rows too large");
+  if (!seed || !out_token) return fail(TS_ERR_INVALID_ARG, "seed and out_token are required");
   int dev;
   const int rc = check_device(&dev);
   if (rc != TS_OK) return rc;

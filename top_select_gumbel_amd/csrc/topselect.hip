@@ -2726,14 +2726,14 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
            void* stream, float* out_logp = nullptr, float* out_lse = nullptr,
            const float* minp = nullptr, const int32_t* lengths = nullptr, const int32_t* offsets = nullptr,
            int order = TS_ORDER_INDEX) {
-  if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (V < 1 || V > TS_MAX_VOCAB) return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)V);
   if (stride < V) return fail(TS_ERR_INVALID_ARG, "row_stride %lld < vocab %lld", (long long)stride, (long long)V);
+  if (rows == 0) return TS_OK;   // an empty batch: nothing to read or write
+  if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows > 0x7FFFFFFF) return fail(TS_ERR_INVALID_ARG, "rows too large");
   Plan pl;
   if (!make_plan(rows, V, pl)) return fail(TS_ERR_INVALID_ARG, "rows x chunks too large");
-  if (rows == 0) return TS_OK;
   if (!ws) return fail(TS_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)ws & 255u) != 0) return fail(TS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < pl.total)
