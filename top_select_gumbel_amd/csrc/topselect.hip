@@ -1278,26 +1278,42 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sd);
     const uint32_t k1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sd >> 32));
     const float inv_t = 1.0f / rp.t;   // one rounding per row instead of a division per token
+    // Branch-free over the slots, so that the eight Philox chains can interleave: every
+    // lane draws for every slot (a lane past its range draws for ids it then ignores), and
+    // the argmax keeps (score, lowest id) through selects, a tree within each quad. The
+    // winner does not depend on the order of the comparisons (ties compare ids).
+    auto better = [](float sa, int32_t ia, float sb, int32_t ib) {
+      return sb > sa || (sb == sa && ib < ia);
+    };
     float bs = -INFINITY;
     int32_t bi = 0x7FFFFFFF;
 #pragma unroll
     for (int s = 0; s < kS1; ++s) {
       const int q = q_lo + s * 64 + l;
       const int nv = nvalid(s);
-      if (nv > 0) {
-        const uint32_t tok0 = (uint32_t)(c0 + 4 * q);
-        const uint4 wd = philox4x32_10(tok0 >> 2, (uint32_t)r, k0, k1);
-        const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+      const uint32_t tok0 = (uint32_t)(c0 + 4 * q);
+      const uint4 wd = philox4x32_10(tok0 >> 2, (uint32_t)r, k0, k1);
+      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+      float sc[4];
+      int32_t id[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (e < nv) {
-            const float g = gumbel_from_uniform(uniform_from_word(words[e]));
-            const float sc = (xval(s, e) - m_w) * inv_t + g;
-            const int32_t id = (int32_t)(tok0 + e);
-            if (sc > bs || (sc == bs && id < bi)) { bs = sc; bi = id; }
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float g = gumbel_from_uniform(uniform_from_word(words[e]));
+        sc[e] = e < nv ? (xval(s, e) - m_w) * inv_t + g : -INFINITY;
+        id[e] = e < nv ? (int32_t)(tok0 + e) : 0x7FFFFFFF;
       }
+      const bool b01 = better(sc[0], id[0], sc[1], id[1]);
+      const float s01 = b01 ? sc[1] : sc[0];
+      const int32_t i01 = b01 ? id[1] : id[0];
+      const bool b23 = better(sc[2], id[2], sc[3], id[3]);
+      const float s23 = b23 ? sc[3] : sc[2];
+      const int32_t i23 = b23 ? id[3] : id[2];
+      const bool bq = better(s01, i01, s23, i23);
+      const float sq = bq ? s23 : s01;
+      const int32_t iq = bq ? i23 : i01;
+      const bool bb = better(bs, bi, sq, iq);
+      bs = bb ? sq : bs;
+      bi = bb ? iq : bi;
     }
     wave_argmax(bs, bi);
     best_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bs), 63));
