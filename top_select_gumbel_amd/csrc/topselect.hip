@@ -105,14 +105,14 @@ struct WaveInfo {
   uint32_t kmax_idx;  // lowest id holding kmax (GREEDY)
   float best_s;       // FULL sampling: best score relative to kmax's value
   int32_t best_idx;
-  uint32_t kmin;      // NUCLEUS rows: smallest key among the wave's elements
+  uint32_t pad;
 };
 static_assert(sizeof(WaveInfo) == 32, "WaveInfo layout");
 constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Per-row state of the nucleus passes. Histograms over the first radix digit of the row's
-// keys (the bits below the common prefix of its smallest and largest key): token counts,
+// Per-row state of the nucleus passes. Histograms over the nucleus bins (value-linear bins in
+// a window below the row maximum, and one bin for everything below it): token counts,
 // counts of tokens min-p keeps, exact fixed-point masses. Then the best Gumbel score of the
 // kept tokens above the cut bin, as (ordered score << 32 | ~id) so that the maximum prefers
 // the lowest id on equal scores, and the number of cut-bin tokens listed (the list itself
@@ -1323,19 +1323,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   if (MODE == kModeTopp && P.out_mask) {
     fill_bytes_nt<kT1>(P.out_mask + (int64_t)r * P.V + c0, n, (path == kPathFull) ? (uint8_t)1 : (uint8_t)0);
   }
-  uint32_t kmin_w = 0xFFFFFFFFu;
   if (path == kPathNucleus) {
-    // the wave's smallest key (the nucleus pass bins keys below the row's common prefix) and
     // this workgroup's share of zeroing the row's nucleus histograms
-    float fmn = INFINITY;
-#pragma unroll
-    for (int s = 0; s < kS1; ++s) {
-      const int nv = nvalid(s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < nv) fmn = fminf(fmn, xval(s, e));
-    }
-    kmin_w = wave_min(f2key(fmn));
     uint4* z = reinterpret_cast<uint4*>(P.nuc + r);
     const int nz = (int)(sizeof(NucRow) / sizeof(uint4));
     const int per = (nz + P.chunks - 1) / P.chunks;
@@ -1350,7 +1339,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     wi.kmax_idx = kmax_idx;
     wi.best_s = best_s;
     wi.best_idx = best_idx;
-    wi.kmin = kmin_w;
+    wi.pad = 0u;
     P.info[seg] = wi;
   }
 }
@@ -1872,8 +1861,8 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 // ------------------------------------------------------------------ nucleus pass
 // Rows with top-k off and top-p or min-p on (NUCLEUS): rows x chunks workgroups, run after
 // the stream kernel. Each weighs its chunk against the row maximum (the same fixed-point
-// masses as the exact top-p select: S = 63 - bitlen(V)), bins the keys by the first radix
-// digit below the row's common key prefix, and adds per bin the token count, the count min-p
+// masses as the exact top-p select: S = 63 - bitlen(V)), bins the tokens by value in the
+// window below the row maximum (nuc_bin), and adds per bin the token count, the count min-p
 // keeps, the mass and - when sampling - the best Gumbel score of the kept tokens into the
 // row's NucRow. The row kernel then needs only the bin where the nucleus ends.
 // f(x, i) for the n elements of a chunk starting at `row` (NT threads; float4 loads, four
@@ -1907,6 +1896,31 @@ __device__ __forceinline__ void chunk_visit(const float* row, int n, F f) {
   }
 }
 
+// Bins of the nucleus passes: value-linear over the window [lo, m] below the row maximum m,
+// bins 1 .. kNucBins - 1, and bin 0 for every token below lo (and -inf). (Each workgroup adds
+// its non-empty bins to the row's histograms with global atomics, so the bin count is kept
+// moderate.) lo = m + T (ln((1 - p)
+// / V) - 1): a token below it has weight exp((x - m) / T) < (1 - p) / (e V), so the tokens of
+// bin 0 together hold less than (1 - p) / e of the total mass (the maximum's weight is 1) and
+// the nucleus's last token lies in the window; its bin then holds few tokens. Only the size
+// of that bin depends on this bound, not the result (any bin is cut exactly). The bin is a
+// monotone function of x, so every bin is a contiguous key range. p == 1 (no cut): one bin.
+constexpr int kNucBins = 1024;   // bins 0 .. kNucBins - 1 of the kDBins a NucRow holds
+struct NucBin {
+  float lo;
+  float scale;
+};
+__device__ __forceinline__ NucBin nuc_bin_params(float m, float p, float t, int V) {
+  if (!(p < 1.0f)) return NucBin{-INFINITY, 0.0f};
+  const double span = (double)t * (1.0 - log((1.0 - (double)p) / (double)V));   // > 0
+  return NucBin{(float)((double)m - span), (float)((double)(kNucBins - 1) / span)};
+}
+__device__ __forceinline__ uint32_t nuc_bin(float x, const NucBin& nb) {
+  if (!(x >= nb.lo)) return 0u;
+  const float f = (x - nb.lo) * nb.scale;   // >= 0; a monotone function of x
+  return min(1u + (uint32_t)f, (uint32_t)(kNucBins - 1));
+}
+
 constexpr int kNT = 512;   // threads of the histogram pass (its LDS allows 4 workgroups per CU)
 struct SmemN {
   uint32_t cnt[kDBins];
@@ -1915,11 +1929,11 @@ struct SmemN {
   uint32_t red[4 * (kNT / 64)];
 };
 
-// The row plan and key range of a NUCLEUS row from its wave summaries (common to the nucleus
+// The row plan and maximum key of a NUCLEUS row from its wave summaries (common to the nucleus
 // kernels). Returns false for rows that are not NUCLEUS or that the row kernel rejects.
 struct NucPlan {
   RowPlan rp;
-  uint32_t kmax, kmin;
+  uint32_t kmax;
 };
 template <int MODE, int NT, int NW>
 __device__ __forceinline__ bool nucleus_plan(const Params& P, int r, uint32_t* red, NucPlan& np) {
@@ -1927,16 +1941,14 @@ __device__ __forceinline__ bool nucleus_plan(const Params& P, int r, uint32_t* r
   if (np.rp.path != kPathNucleus) return false;        // uniform
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
-  uint32_t kmax = 0, kmin = 0xFFFFFFFFu, flags = 0, dummy = 0u;
+  uint32_t kmax = 0, dummy = 0u, dummy2 = 0xFFFFFFFFu, flags = 0;
   for (int i = threadIdx.x; i < nseg; i += NT) {
     const WaveInfo wi = inf[i];
     kmax = max(kmax, wi.kmax);
-    kmin = min(kmin, wi.kmin);
     flags |= wi.flags;
   }
-  block_reduce4<NW>(kmax, dummy, kmin, flags, red);
+  block_reduce4<NW>(kmax, dummy, dummy2, flags, red);
   np.kmax = kmax;
-  np.kmin = kmin;
   return !((flags & kFlagNan) || kmax >= kKeyPosInf || kmax <= kKeyNegInf);
 }
 
@@ -1954,7 +1966,7 @@ __global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   NucPlan np;
   if (!nucleus_plan<MODE, kNT, kNT / 64>(P, r, sm.red, np)) return;   // uniform
   const RowPlan& rp = np.rp;
-  const uint32_t kmax = np.kmax, kmin = np.kmin;
+  const uint32_t kmax = np.kmax;
   for (int i = threadIdx.x; i < kDBins; i += kNT) {
     sm.cnt[i] = 0u;
     sm.cok[i] = 0u;
@@ -1963,27 +1975,50 @@ __global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   const float m = key2f(kmax);
   const double c2 = kLog2e / (double)rp.t;
   const int S = 63 - bitlen((uint32_t)P.V);
-  const Digit g = first_digit(kmax, kmin);
+  const NucBin nb = nuc_bin_params(m, rp.p, rp.t, P.V);
   const bool minp_on = rp.minp > 0.0f;
   const int c0 = c * P.chunk_len;
   const int n = max(0, min(P.chunk_len, P.V - c0));
   const float* row = P.x + (int64_t)r * P.stride + c0;
   bar();
+  // Bin 0 (below the window) holds most of a spread row's tokens: its count, kept count and
+  // mass are summed in registers and added once per wave instead of by LDS atomics on one
+  // address.
+  uint32_t z0c = 0, z0k = 0;
+  uint64_t z0m = 0;
   chunk_visit<kNT>(row, n, [&](float x, uint32_t) {
     const uint32_t key = f2key(x);
-    const uint32_t bin = (key >> g.sh) & g.dm;
+    const uint32_t bin = nuc_bin(x, nb);
     const float w = weight32(key, m, c2);
-    hist_add(sm.cnt, bin);
-    atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)mass32_of(w, S));
-    if (!minp_on || w >= rp.minp) atomicAdd(&sm.cok[bin], 1u);
+    const uint64_t q = mass32_of(w, S);
+    const bool kp = !minp_on || w >= rp.minp;
+    if (bin == 0u) {
+      z0c += 1u;
+      z0m += q;
+      z0k += kp ? 1u : 0u;
+    } else {
+      hist_add(sm.cnt, bin);
+      atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)q);
+      if (kp) atomicAdd(&sm.cok[bin], 1u);
+    }
   });
+  {
+    const uint32_t wc = wave_total(wave_incl_scan(z0c));
+    const uint32_t wk = wave_total(wave_incl_scan(z0k));
+    const uint64_t wm = readlane64(wave_incl_scan64(z0m), 63);
+    if (lane() == 0 && wc) {
+      atomicAdd(&sm.cnt[0], wc);
+      atomicAdd(&sm.cok[0], wk);
+      atomicAdd((unsigned long long*)&sm.mass[0], (unsigned long long)wm);
+    }
+  }
   bar();
   NucRow* nr = P.nuc + r;
-  for (int i = threadIdx.x; i < kDBins; i += kNT) {
+  for (int i = threadIdx.x; i < kNucBins; i += kNT) {
     const uint32_t cn = sm.cnt[i];
     if (cn) {
       atomicAdd(&nr->cnt[i], cn);
-      const uint32_t co = sm.cok[i];
+      const uint32_t co = minp_on ? sm.cok[i] : 0u;   // without min-p the row kernel uses cnt
       if (co) atomicAdd(&nr->cok[i], co);
       atomicAdd((unsigned long long*)&nr->mass[i], (unsigned long long)sm.mass[i]);
     }
@@ -2019,7 +2054,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   if (!nucleus_plan<MODE, kT1, kW1>(P, r, sm.red, np)) return;
   const RowPlan& rp = np.rp;
   NucRow* nr = P.nuc + r;
-  const Digit g = first_digit(np.kmax, np.kmin);
+  const NucBin nb = nuc_bin_params(key2f(np.kmax), rp.p, rp.t, P.V);
   int cut = -1;
   if (rp.p != 1.0f) {
     constexpr int kB = kDBins / kT1;                   // 8 bins per thread, thread t: 8t .. 8t+7
@@ -2090,7 +2125,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
     for (int s = 0; s < kQ; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (valid(s, e) && (int)((f2key(elem(s, e)) >> g.sh) & g.dm) == cut) ++mine;
+        if (valid(s, e) && (int)nuc_bin(elem(s, e), nb) == cut) ++mine;
   }
   const uint32_t wincl = wave_incl_scan(mine);
   const uint32_t wtot = wave_total(wincl);
@@ -2114,7 +2149,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t key = f2key(elem(s, e));
-      const int bin = (int)((key >> g.sh) & g.dm);
+      const int bin = (int)nuc_bin(elem(s, e), nb);
       mem[e] = false;
       if (!valid(s, e)) continue;
       if (bin == cut) {
@@ -2174,12 +2209,7 @@ template <int MODE>
 __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
                                                uint64_t seed, Smem& sm, double lse) {
   const int nseg = P.chunks * kW1;
-  const WaveInfo* inf = P.info + (int64_t)r * nseg;
-  uint32_t kmin = 0xFFFFFFFFu;
-  for (int i = threadIdx.x; i < nseg; i += kRT) kmin = min(kmin, inf[i].kmin);
-  kmin = block_min_u32<kRW>(kmin, sm.red);
   const NucRow* nr = P.nuc + r;
-  const Digit g = first_digit(kmax, kmin);
   const uint32_t V = (uint32_t)P.V;
   const float m = key2f(kmax);
   const float t = rp.t;
@@ -2198,7 +2228,7 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
     const int i = (int)threadIdx.x + j * kRT;
     hc[j] = nr->cnt[i];
     hm[j] = nr->mass[i];
-    hk[j] = nr->cok[i];
+    hk[j] = minp_on ? nr->cok[i] : hc[j];   // the histogram pass fills cok only with min-p
   }
   uint64_t zh = 0, zl = 0;
 #pragma unroll
@@ -2238,9 +2268,14 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
       }
     }
     bar();
-    const uint32_t bprefix = (g.prefix << (g.lo - g.sh)) | (uint32_t)cut;   // key >> g.sh of the bin
-    const uint32_t base_key = bprefix << g.sh;
-    const uint32_t top_key = g.sh == 0 ? base_key : (base_key | ((1u << g.sh) - 1u));
+    // the cut bin's key range, from its tokens (a bin is a contiguous key range)
+    uint32_t top_key = 0u, base_key = 0xFFFFFFFFu;
+    for (uint32_t i = threadIdx.x; i < ncut; i += kRT) {
+      top_key = max(top_key, sm.ckey[i]);
+      base_key = min(base_key, sm.ckey[i]);
+    }
+    top_key = block_max_u32<kRW>(top_key, sm.red);
+    base_key = block_min_u32<kRW>(base_key, sm.red);
     uint32_t kept_unused;
     sp = select_mass<false>(LdsVis{sm.ckey, sm.cidx, ncut}, wmass, target, ncut, top_key, base_key, 0u, V - 1,
                             sm, kept_unused, false, ma, n_above);
