@@ -1906,6 +1906,7 @@ __device__ __forceinline__ void chunk_visit(const float* row, int n, F f) {
 // of that bin depends on this bound, not the result (any bin is cut exactly). The bin is a
 // monotone function of x, so every bin is a contiguous key range. p == 1 (no cut): one bin.
 constexpr int kNucBins = 1024;   // bins 0 .. kNucBins - 1 of the kDBins a NucRow holds
+static_assert(kNucBins % kT1 == 0 && kNucBins <= kDBins, "nucleus bins: whole per-thread groups");
 struct NucBin {
   float lo;
   float scale;
@@ -1967,7 +1968,7 @@ __global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   if (!nucleus_plan<MODE, kNT, kNT / 64>(P, r, sm.red, np)) return;   // uniform
   const RowPlan& rp = np.rp;
   const uint32_t kmax = np.kmax;
-  for (int i = threadIdx.x; i < kDBins; i += kNT) {
+  for (int i = threadIdx.x; i < kNucBins; i += kNT) {
     sm.cnt[i] = 0u;
     sm.cok[i] = 0u;
     sm.mass[i] = 0ull;
@@ -2057,7 +2058,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   const NucBin nb = nuc_bin_params(key2f(np.kmax), rp.p, rp.t, P.V);
   int cut = -1;
   if (rp.p != 1.0f) {
-    constexpr int kB = kDBins / kT1;                   // 8 bins per thread, thread t: 8t .. 8t+7
+    constexpr int kB = kNucBins / kT1;                 // 4 bins per thread, thread t: 4t .. 4t+3
     uint64_t ms[kB], tsum = 0;
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
