@@ -111,20 +111,22 @@ static_assert(sizeof(WaveInfo) == 32, "WaveInfo layout");
 constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Per-row state of the nucleus passes. Histograms over the nucleus bins (value-linear bins in
-// a window below the row maximum, and one bin for everything below it): token counts,
-// counts of tokens min-p keeps, exact fixed-point masses. Then the best Gumbel score of the
+// Per-row state of the nucleus passes. The exact fixed-point mass of every nucleus bin
+// (value-linear bins in a window below the row maximum, and one bin for everything below
+// it), then the counts of the tokens above the cut bin (and those min-p keeps), the best Gumbel score of the
 // kept tokens above the cut bin, as (ordered score << 32 | ~id) so that the maximum prefers
 // the lowest id on equal scores, and the number of cut-bin tokens listed (the list itself
 // lives in the row's candidate slices, which nucleus rows leave unused).
+constexpr int kNucBins = 1024;   // nucleus bins (value-linear window below the maximum, and bin 0)
 struct NucRow {
-  uint32_t cnt[kDBins];
-  uint32_t cok[kDBins];
-  uint64_t mass[kDBins];
-  uint64_t best;
-  uint32_t nlist;
-  uint32_t pad;
+  uint64_t mass[kNucBins];     // exact fixed-point mass per bin
+  uint64_t best;               // best (ordered score << 32 | ~id) of the kept tokens above the cut bin
+  uint32_t nlist;              // tokens of the cut bin, listed by the cut pass
+  uint32_t nabove;             // tokens in bins above the cut bin
+  uint32_t kabove;             // of those, the ones min-p keeps (all of them without min-p)
+  uint32_t pad[3];
 };
+static_assert(sizeof(NucRow) % 16 == 0, "NucRow is zeroed in 16-byte words");
 
 struct Params {
   const float* x;
@@ -1862,9 +1864,9 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 // Rows with top-k off and top-p or min-p on (NUCLEUS): rows x chunks workgroups, run after
 // the stream kernel. Each weighs its chunk against the row maximum (the same fixed-point
 // masses as the exact top-p select: S = 63 - bitlen(V)), bins the tokens by value in the
-// window below the row maximum (nuc_bin), and adds per bin the token count, the count min-p
-// keeps, the mass and - when sampling - the best Gumbel score of the kept tokens into the
-// row's NucRow. The row kernel then needs only the bin where the nucleus ends.
+// window below the row maximum (nuc_bin), and adds each bin's mass into the row's NucRow.
+// The cut pass then finds the bin where the nucleus ends and counts, draws and lists the
+// tokens; the row kernel finishes the cut bin.
 // f(x, i) for the n elements of a chunk starting at `row` (NT threads; float4 loads, four
 // per thread in flight, when the chunk is 16-byte aligned).
 template <int NT, class F>
@@ -1905,8 +1907,7 @@ __device__ __forceinline__ void chunk_visit(const float* row, int n, F f) {
 // the nucleus's last token lies in the window; its bin then holds few tokens. Only the size
 // of that bin depends on this bound, not the result (any bin is cut exactly). The bin is a
 // monotone function of x, so every bin is a contiguous key range. p == 1 (no cut): one bin.
-constexpr int kNucBins = 1024;   // bins 0 .. kNucBins - 1 of the kDBins a NucRow holds
-static_assert(kNucBins % kT1 == 0 && kNucBins <= kDBins, "nucleus bins: whole per-thread groups");
+static_assert(kNucBins % kT1 == 0 && kNucBins % kRT == 0 && kNucBins <= kDBins, "nucleus bins");
 struct NucBin {
   float lo;
   float scale;
@@ -1924,9 +1925,7 @@ __device__ __forceinline__ uint32_t nuc_bin(float x, const NucBin& nb) {
 
 constexpr int kNT = 512;   // threads of the histogram pass (its LDS allows 4 workgroups per CU)
 struct SmemN {
-  uint32_t cnt[kDBins];
-  uint32_t cok[kDBins];
-  uint64_t mass[kDBins];
+  uint64_t mass[kNucBins];
   uint32_t red[4 * (kNT / 64)];
 };
 
@@ -1968,61 +1967,33 @@ __global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   if (!nucleus_plan<MODE, kNT, kNT / 64>(P, r, sm.red, np)) return;   // uniform
   const RowPlan& rp = np.rp;
   const uint32_t kmax = np.kmax;
-  for (int i = threadIdx.x; i < kNucBins; i += kNT) {
-    sm.cnt[i] = 0u;
-    sm.cok[i] = 0u;
-    sm.mass[i] = 0ull;
-  }
+  for (int i = threadIdx.x; i < kNucBins; i += kNT) sm.mass[i] = 0ull;
   const float m = key2f(kmax);
   const double c2 = kLog2e / (double)rp.t;
   const int S = 63 - bitlen((uint32_t)P.V);
   const NucBin nb = nuc_bin_params(m, rp.p, rp.t, P.V);
-  const bool minp_on = rp.minp > 0.0f;
   const int c0 = c * P.chunk_len;
   const int n = max(0, min(P.chunk_len, P.V - c0));
   const float* row = P.x + (int64_t)r * P.stride + c0;
   bar();
-  // Bin 0 (below the window) holds most of a spread row's tokens: its count, kept count and
-  // mass are summed in registers and added once per wave instead of by LDS atomics on one
-  // address.
-  uint32_t z0c = 0, z0k = 0;
+  // Bin 0 (below the window) holds most of a spread row's tokens: its mass is summed in
+  // registers and added once per wave instead of by LDS atomics on one address.
   uint64_t z0m = 0;
   chunk_visit<kNT>(row, n, [&](float x, uint32_t) {
-    const uint32_t key = f2key(x);
     const uint32_t bin = nuc_bin(x, nb);
-    const float w = weight32(key, m, c2);
-    const uint64_t q = mass32_of(w, S);
-    const bool kp = !minp_on || w >= rp.minp;
-    if (bin == 0u) {
-      z0c += 1u;
-      z0m += q;
-      z0k += kp ? 1u : 0u;
-    } else {
-      hist_add(sm.cnt, bin);
-      atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)q);
-      if (kp) atomicAdd(&sm.cok[bin], 1u);
-    }
+    const uint64_t q = mass32_of(weight32(f2key(x), m, c2), S);
+    if (bin == 0u) z0m += q;
+    else if (q) atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)q);
   });
   {
-    const uint32_t wc = wave_total(wave_incl_scan(z0c));
-    const uint32_t wk = wave_total(wave_incl_scan(z0k));
     const uint64_t wm = readlane64(wave_incl_scan64(z0m), 63);
-    if (lane() == 0 && wc) {
-      atomicAdd(&sm.cnt[0], wc);
-      atomicAdd(&sm.cok[0], wk);
-      atomicAdd((unsigned long long*)&sm.mass[0], (unsigned long long)wm);
-    }
+    if (lane() == 0 && wm) atomicAdd((unsigned long long*)&sm.mass[0], (unsigned long long)wm);
   }
   bar();
   NucRow* nr = P.nuc + r;
   for (int i = threadIdx.x; i < kNucBins; i += kNT) {
-    const uint32_t cn = sm.cnt[i];
-    if (cn) {
-      atomicAdd(&nr->cnt[i], cn);
-      const uint32_t co = minp_on ? sm.cok[i] : 0u;   // without min-p the row kernel uses cnt
-      if (co) atomicAdd(&nr->cok[i], co);
-      atomicAdd((unsigned long long*)&nr->mass[i], (unsigned long long)sm.mass[i]);
-    }
+    const uint64_t q = sm.mass[i];
+    if (q) atomicAdd((unsigned long long*)&nr->mass[i], (unsigned long long)q);
   }
 }
 
@@ -2142,6 +2113,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   const uint32_t cap_list = (uint32_t)min((int64_t)kLdsCand, (int64_t)nseg * P.cap_w);
   uint32_t at = sm.res[0] + (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase) + wincl - mine;
   uint64_t best = 0;
+  uint64_t n_up = 0, k_up = 0;   // this thread's tokens above the cut bin, and those min-p keeps
   const int w = wave(), l = lane();
 #pragma unroll
   for (int s = 0; s < kQ; ++s) {
@@ -2158,6 +2130,8 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
         ++at;
       } else if (bin > cut) {
         mem[e] = !minp_on || weight32(key, m, c2) >= rp.minp;
+        ++n_up;
+        k_up += mem[e] ? 1u : 0u;
       }
     }
     if (MODE == kModeSample) {
@@ -2191,6 +2165,12 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
         if (mem[e]) mrow[id0 - c0 + e] = 1;
     }
   }
+  // the workgroup's tokens above the cut bin (and those min-p keeps): one atomic each
+  block_sum2_u64<kW1>(n_up, k_up, sm.red64);
+  if (threadIdx.x == 0 && n_up) {
+    atomicAdd(&nr->nabove, (uint32_t)n_up);
+    atomicAdd(&nr->kabove, (uint32_t)k_up);
+  }
   if (MODE == kModeSample) {
     uint32_t hi = (uint32_t)(best >> 32);
     hi = block_max_u32<kW1>(hi, sm.red);
@@ -2219,26 +2199,18 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
   const bool minp_on = rp.minp > 0.0f;
   auto wmass = [&](uint32_t rk) { return mass32_of(weight32(rk, m, c2), S); };
   auto ok = [&](uint32_t rk) { return !minp_on || weight32(rk, m, c2) >= rp.minp; };
-  // the histograms in one batch of loads: counts and masses into LDS (for the search), the
-  // kept counts in registers
-  constexpr int kPerT = kDBins / kRT;
-  uint32_t hc[kPerT], hk[kPerT];
-  uint64_t hm[kPerT];
-#pragma unroll
-  for (int j = 0; j < kPerT; ++j) {
-    const int i = (int)threadIdx.x + j * kRT;
-    hc[j] = nr->cnt[i];
-    hm[j] = nr->mass[i];
-    hk[j] = minp_on ? nr->cok[i] : hc[j];   // the histogram pass fills cok only with min-p
-  }
+  // the masses into LDS for the search (the bins past kNucBins and the count histogram stay
+  // zero: the cut pass counted the tokens itself)
+  constexpr int kPerT = kNucBins / kRT;
   uint64_t zh = 0, zl = 0;
 #pragma unroll
   for (int j = 0; j < kPerT; ++j) {
     const int i = (int)threadIdx.x + j * kRT;
-    sm.hist[i] = hc[j];
-    sm.mhi[i] = hm[j];
-    zh += hm[j];
+    const uint64_t q = nr->mass[i];
+    sm.mhi[i] = q;
+    zh += q;
   }
+  const uint32_t n_list = nr->nlist, n_up = nr->nabove, k_up = nr->kabove;
   block_sum2_u64<kRW>(zh, zl, sm.red64);
   int cut = -1;                 // the bin holding the nucleus's last token; -1: no cut (p == 1)
   uint32_t ncut = 0;            // tokens in the cut bin
@@ -2247,8 +2219,8 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
     const uint64_t target = topp_target(rp.p, zh);
     search_mass(sm, target, 0ull);   // reads and clears the histograms
     cut = (int)sm.res[0];
-    const uint32_t n_above = sm.res[1];
-    ncut = sm.res[2];
+    const uint32_t n_above = n_up;   // counted by the cut pass for the same cut bin
+    ncut = n_list;
     const uint64_t ma = sm.res64[0];
     if (ncut > (uint32_t)kLdsCand) return false;
     const uint2* list = P.cand + (int64_t)r * nseg * P.cap_w;   // ncut entries, any order
@@ -2283,10 +2255,7 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
   }
   if (MODE == kModeTopp) {
     // kept: tokens of bins above the cut that min-p keeps, plus the cut bin's kept members
-    uint64_t c = 0, z = 0;
-#pragma unroll
-    for (int j = 0; j < kPerT; ++j)
-      if ((int)threadIdx.x + j * kRT > cut) c += hk[j];
+    uint64_t c = threadIdx.x == 0 ? (uint64_t)k_up : 0ull, z = 0;
     uint8_t* mrow = P.out_mask ? P.out_mask + (int64_t)r * P.V : nullptr;
     for (uint32_t i = threadIdx.x; i < ncut; i += kRT) {
       if (sel_member(sp, sm.ckey[i], sm.cidx[i]) && ok(sm.ckey[i])) {
