@@ -2212,13 +2212,13 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
   }
   const uint32_t n_list = nr->nlist, n_up = nr->nabove, k_up = nr->kabove;
   block_sum2_u64<kRW>(zh, zl, sm.red64);
-  int cut = -1;                 // the bin holding the nucleus's last token; -1: no cut (p == 1)
-  uint32_t ncut = 0;            // tokens in the cut bin
+  uint32_t ncut = 0;            // tokens in the cut bin (the bin holding the nucleus's last token)
   Sel sp = sel_all();
   if (rp.p != 1.0f) {
     const uint64_t target = topp_target(rp.p, zh);
-    search_mass(sm, target, 0ull);   // reads and clears the histograms
-    cut = (int)sm.res[0];
+    // the mass above the cut bin (the cut pass found the same bin); the search also clears
+    // the LDS histograms for the select below
+    search_mass(sm, target, 0ull);
     const uint32_t n_above = n_up;   // counted by the cut pass for the same cut bin
     ncut = n_list;
     const uint64_t ma = sm.res64[0];
