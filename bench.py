@@ -459,6 +459,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "region_us_per_call": region_ms * 1e3,
+        # HBM passes over the logits per call (measured traffic / algorithmic bytes), from the
+        # committed PMC summary while it matches the kernel sources
+        "passes_per_row": None if traffic is None else traffic / BYTES_PER_CALL,
         "kernel_us": {"avg": avg * 1e3, "median": med * 1e3, "p10": float(np.percentile(kern_ms, 10)) * 1e3,
                       "p90": float(np.percentile(kern_ms, 90)) * 1e3},
         "warm_kernel_us_median": float(np.median(warm_ms)) * 1e3,
