@@ -51,6 +51,7 @@
 #include <atomic>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "topselect.h"
@@ -2544,35 +2545,37 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
         if (pre) atomicAdd(&sm.hist[(v.x >> g0.sh) & g0.dm], 1u);
       };
       {
-        // Wave w copies slices w, w + kRW, ...: lane l takes slot l of each (coalesced). Per
-        // batch of kGatherB slices the offsets are read first, then every load is issued,
-        // then the candidates are written; slices holding more than 64 finish afterwards.
-        for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
-          uint32_t o[kGatherB], cnt[kGatherB];
+        // Wave w copies slices w, w + kRW, ...: lane l takes slots l, l + 64, ... of each
+        // (coalesced). Per batch of kGatherB slices the offsets are read first, then every load
+        // is issued (two per slice and lane when a slice of the batch holds more than 64, so
+        // that such slices cost no second round trip), then the candidates are written; slices
+        // holding more than 64 * NL finish afterwards.
+        const uint32_t j = (uint32_t)lane();
+        auto batch = [&](const uint2* gs, const uint32_t* o, const uint32_t* cnt, auto nl) {
+          constexpr uint32_t NL = decltype(nl)::value;
+          uint2 v[kGatherB][NL];
 #pragma unroll
           for (int u = 0; u < kGatherB; ++u) {
-            const int sl = min(sb + u * kRW, nseg);   // slice nseg has no candidates
-            o[u] = sm.segoff[sl];
-            cnt[u] = sm.segoff[min(sl + 1, nseg)] - o[u];
-          }
-          const uint2* gs = P.cand + ((int64_t)r * nseg + sb) * P.cap_w;
-          const uint32_t j = (uint32_t)lane();
-          uint2 v[kGatherB];
 #pragma unroll
-          for (int u = 0; u < kGatherB; ++u) {
-            v[u] = make_uint2(0, 0);
-            if (j < cnt[u]) v[u] = gs[(int64_t)u * kRW * P.cap_w + j];
+            for (uint32_t e = 0; e < NL; ++e) {
+              const uint32_t jj = 64u * e + j;
+              v[u][e] = jj < cnt[u] ? gs[(int64_t)u * kRW * P.cap_w + jj] : make_uint2(0, 0);
+            }
           }
           bool more = false;
 #pragma unroll
           for (int u = 0; u < kGatherB; ++u) {
-            if (j < cnt[u]) put(o[u] + j, v[u]);
-            more |= cnt[u] > 64u;
+#pragma unroll
+            for (uint32_t e = 0; e < NL; ++e) {
+              const uint32_t jj = 64u * e + j;
+              if (jj < cnt[u]) put(o[u] + jj, v[u][e]);
+            }
+            more |= cnt[u] > 64u * NL;
           }
-          if (more) {   // wave-uniform: some slice of the batch holds more than 64 candidates
+          if (more) {   // wave-uniform: some slice of the batch holds more than 64 * NL candidates
 #pragma unroll
             for (int u = 0; u < kGatherB; ++u) {
-              for (uint32_t j0 = 64u; j0 < cnt[u]; j0 += 256u) {   // 4 loads in flight per lane
+              for (uint32_t j0 = 64u * NL; j0 < cnt[u]; j0 += 256u) {   // 4 loads in flight per lane
                 uint2 w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -2587,6 +2590,19 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
               }
             }
           }
+        };
+        for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
+          uint32_t o[kGatherB], cnt[kGatherB], mx = 0;
+#pragma unroll
+          for (int u = 0; u < kGatherB; ++u) {
+            const int sl = min(sb + u * kRW, nseg);   // slice nseg has no candidates
+            o[u] = sm.segoff[sl];
+            cnt[u] = sm.segoff[min(sl + 1, nseg)] - o[u];
+            mx = max(mx, cnt[u]);
+          }
+          const uint2* gs = P.cand + ((int64_t)r * nseg + sb) * P.cap_w;
+          if (mx > 64u) batch(gs, o, cnt, std::integral_constant<uint32_t, 2>{});
+          else batch(gs, o, cnt, std::integral_constant<uint32_t, 1>{});
         }
       }
       bar();
