@@ -88,3 +88,31 @@ def test_unaligned_rows_and_ragged_tails(v, pad):
     tok, st3 = ts.ts_sample_rows(xs, dev(k), dev(p), dev(t), dev(seeds))
     torch.cuda.synchronize()
     check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, f"unaligned {v}")
+
+
+def test_long_rows_flat_gather_all_entry_points():
+    """Rows of 400,003 logits (49 chunks, 196 wave slices: more than one gather batch per wave)
+    with candidate totals from a few hundred to several thousand, so that the row kernel's flat
+    gather runs with each of its per-thread item counts, in all three entry points."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(4003)
+    rows, v = 6, 400003
+    x = (rng.standard_normal((rows, v)) * 1.5).astype(np.float32)
+    x[3] = np.round(x[3], 2)                     # ties at the top-k boundary
+    k = np.array([1, 64, 700, 1500, 2048, 2048], np.int32)
+    p = np.array([0.9, 0.8, 0.95, 1.0, 0.7, 0.99], np.float32)
+    t = np.array([1.0, 0.8, 1.2, 1.0, 0.6, 1.4], np.float32)
+    seeds = rng.integers(0, 2 ** 64, rows, dtype=np.uint64)
+    banner(f"long rows V={v}: topk")
+    idx, st = ts.ts_topk_select(dev(x), dev(k), 2048)
+    torch.cuda.synchronize()
+    check_topk(x, k, 2048, host(idx), host(st), "long rows")
+    banner(f"long rows V={v}: topp")
+    kept, mask, st2 = ts.ts_topp_mask(dev(x), dev(k), dev(p), dev(t), True)
+    torch.cuda.synchronize()
+    kept = host(kept)
+    check_topp(x, k, p, t, kept, host(mask), host(st2), "long rows")
+    banner(f"long rows V={v}: sample")
+    tok, st3 = ts.ts_sample_rows(dev(x), dev(k), dev(p), dev(t), dev(seeds))
+    torch.cuda.synchronize()
+    check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, "long rows")

@@ -2591,7 +2591,51 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
             }
           }
         };
-        for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
+        // Rows of more slices than one batch per wave covers (long rows): each thread takes
+        // the flat candidate positions tid, tid + kRT, ... instead, finds each one's slice by a
+        // branch-free binary search of the slice offsets in LDS (the E searches interleave),
+        // and issues all its loads at once, so that the gather is one round trip.
+        auto flat = [&](auto ne) {
+          constexpr int E = decltype(ne)::value;
+          const uint2* gr = P.cand + (int64_t)r * nseg * P.cap_w;
+          const uint32_t ns = (uint32_t)nseg;
+          uint32_t sl[E], so[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            sl[e] = 0;
+            so[e] = 0;   // segoff[0]
+          }
+          // the largest slice whose offset is <= f (segoff[nseg] = total exceeds every f)
+          for (uint32_t bb = 1u << (31 - __builtin_clz(ns - 1)); bb > 0; bb >>= 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const uint32_t f = min((uint32_t)(e * kRT) + threadIdx.x, total - 1);
+              const uint32_t t = sl[e] + bb;
+              const uint32_t sv = sm.segoff[min(t, ns)];
+              if (sv <= f) {
+                sl[e] = t;
+                so[e] = sv;
+              }
+            }
+          }
+          uint2 v[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t f = (uint32_t)(e * kRT) + threadIdx.x;
+            v[e] = f < total ? gr[(int64_t)sl[e] * P.cap_w + (f - so[e])] : make_uint2(0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t f = (uint32_t)(e * kRT) + threadIdx.x;
+            if (f < total) put(f, v[e]);
+          }
+        };
+        static_assert(kLdsCand <= 24 * kRT, "flat gather covers the LDS candidate capacity");
+        if (nseg > kRW * kGatherB) {
+          if (total <= 8u * kRT) flat(std::integral_constant<int, 8>{});
+          else if (total <= 16u * kRT) flat(std::integral_constant<int, 16>{});
+          else flat(std::integral_constant<int, 24>{});
+        } else for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
           uint32_t o[kGatherB], cnt[kGatherB], mx = 0;
 #pragma unroll
           for (int u = 0; u < kGatherB; ++u) {
