@@ -2307,7 +2307,8 @@ __device__ __forceinline__ void emit_topk_cand(const Params& P, const RowPlan& r
     emit_value_order(a, nk, (uint32_t)kDBins, orow, kmx, off);
   } else {
     uint32_t run = 0;
-    emit_ordered<4>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
+    // 12 items per thread: up to 6144 candidates per block scan
+    emit_ordered<12>(ntot, [&](uint32_t i, uint32_t& rk, uint32_t& idx) { rk = sm.ckey[i]; idx = sm.cidx[i]; },
                     [&](uint32_t rk, uint32_t idx) { return sel_member(sk, rk, idx); },
                     [&](uint32_t pos, uint32_t idx) { if (pos < kmx) orow[pos] = off + (int32_t)idx; },
                     run, sm);
@@ -2315,7 +2316,10 @@ __device__ __forceinline__ void emit_topk_cand(const Params& P, const RowPlan& r
   for (int i = rp.k_eff + threadIdx.x; i < P.k_max; i += kRT) orow[i] = -1;
 }
 
-template <int MODE>
+// LONG: rows of more wave slices than one gather batch per wave covers (long rows) take the
+// flat gather; it is compiled into a kernel of its own so that the common kernel's code and
+// register allocation stay as they are without it.
+template <int MODE, bool LONG>
 __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   __shared__ Smem sm;
   // With the stream kernel's XCD mapping (rows 8x .. 8x + rows/8 - 1 on XCD x, workgroups
@@ -2631,7 +2635,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           }
         };
         static_assert(kLdsCand <= 24 * kRT, "flat gather covers the LDS candidate capacity");
-        if (nseg > kRW * kGatherB) {
+        if constexpr (LONG) {
           if (total <= 8u * kRT) flat(std::integral_constant<int, 8>{});
           else if (total <= 16u * kRT) flat(std::integral_constant<int, 16>{});
           else flat(std::integral_constant<int, 24>{});
@@ -2645,8 +2649,44 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
             mx = max(mx, cnt[u]);
           }
           const uint2* gs = P.cand + ((int64_t)r * nseg + sb) * P.cap_w;
-          if (mx > 64u) batch(gs, o, cnt, std::integral_constant<uint32_t, 2>{});
-          else batch(gs, o, cnt, std::integral_constant<uint32_t, 1>{});
+          // two loads per slice and lane only in top-k select (its k = 2048 rows publish
+          // slices of 65-128 candidates); the sampling kernels run faster without that code
+          if constexpr (MODE == kModeTopk) {
+            if (mx > 64u) batch(gs, o, cnt, std::integral_constant<uint32_t, 2>{});
+            else batch(gs, o, cnt, std::integral_constant<uint32_t, 1>{});
+          } else {
+            const uint32_t j = (uint32_t)lane();
+            uint2 v[kGatherB];
+#pragma unroll
+            for (int u = 0; u < kGatherB; ++u) {
+              v[u] = make_uint2(0, 0);
+              if (j < cnt[u]) v[u] = gs[(int64_t)u * kRW * P.cap_w + j];
+            }
+            bool more = false;
+#pragma unroll
+            for (int u = 0; u < kGatherB; ++u) {
+              if (j < cnt[u]) put(o[u] + j, v[u]);
+              more |= cnt[u] > 64u;
+            }
+            if (more) {   // wave-uniform: some slice of the batch holds more than 64 candidates
+#pragma unroll
+              for (int u = 0; u < kGatherB; ++u) {
+                for (uint32_t j0 = 64u; j0 < cnt[u]; j0 += 256u) {   // 4 loads in flight per lane
+                  uint2 w[4];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const uint32_t jj = j0 + 64u * e + j;
+                    w[e] = jj < cnt[u] ? gs[(int64_t)u * kRW * P.cap_w + jj] : make_uint2(0, 0);
+                  }
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const uint32_t jj = j0 + 64u * e + j;
+                    if (jj < cnt[u]) put(o[u] + jj, w[e]);
+                  }
+                }
+              }
+            }
+          }
         }
       }
       bar();
@@ -2874,7 +2914,10 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "nucleus cut kernel launch failed: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(ts_row_kernel<MODE>, dim3((unsigned)rows), dim3(kRT), 0, s, P);
+  if (!P.direct && P.chunks * kW1 > kRW * kGatherB)
+    hipLaunchKernelGGL((ts_row_kernel<MODE, true>), dim3((unsigned)rows), dim3(kRT), 0, s, P);
+  else
+    hipLaunchKernelGGL((ts_row_kernel<MODE, false>), dim3((unsigned)rows), dim3(kRT), 0, s, P);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "row kernel launch failed: %s", hipGetErrorString(e));
   return TS_OK;
