@@ -89,7 +89,7 @@ constexpr int kDBins = 1 << kDBits;                 // = 4 bins per row-kernel t
 constexpr int kLdsCand = 12288;                     // candidates the row kernel holds in LDS
 constexpr int kSlab = 8192;                         // row elements per row-streaming Gumbel slab
 constexpr int kValueOrderMax = 8192;                // value-ordered top-k: k_max limit (sort size)
-constexpr int kVisU = 4;                            // LDS items per thread per visitor round
+constexpr int kVisU = 6;                            // LDS items per thread per visitor round
 constexpr int kGatherB = 10;
 constexpr uint32_t kSmallBin = 64;                  // boundary bins up to this size are resolved by one wave                        // wave slices per gather batch
 constexpr int kMaxSeg = 1024;                       // wave slices per row the gather indexes
