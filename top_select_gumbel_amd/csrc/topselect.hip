@@ -90,8 +90,8 @@ constexpr int kLdsCand = 12288;                     // candidates the row kernel
 constexpr int kSlab = 8192;                         // row elements per row-streaming Gumbel slab
 constexpr int kValueOrderMax = 8192;                // value-ordered top-k: k_max limit (sort size)
 constexpr int kVisU = 6;                            // LDS items per thread per visitor round
-constexpr int kGatherB = 10;
-constexpr uint32_t kSmallBin = 64;                  // boundary bins up to this size are resolved by one wave                        // wave slices per gather batch
+constexpr int kGatherB = 10;                        // wave slices per gather batch
+constexpr uint32_t kSmallBin = 64;                  // boundary bins up to this size are resolved by one wave
 constexpr int kMaxSeg = 1024;                       // wave slices per row the gather indexes
 constexpr int kSegPT = kMaxSeg / kRT;               // slice counts scanned per thread
 constexpr int kBPT = kDBins / kRT;                  // histogram bins owned per thread
