@@ -28,9 +28,12 @@ Readings where the page leaves a step open (listed with their reasons in the des
 * Ranks and ties. "Entries greater than a pivot" compare logits, with equal logits ordered
   by id, so the accept test "fewer than k above the candidate" is the candidate's
   canonical rank and the support keeps the lowest ids among equal logits.
-* Second pivot. Halfway between the candidate's logit and the upper bound, taken in logit
-  space in fp32: x1 = fp32(fp32(x0 / 2) + fp32(hi / 2)) (the geometric midpoint of the two
-  probabilities), so that both implementations compare the same fp32 value.
+* Second pivot. Halfway between the candidate's probability and the upper bound of the
+  interval, in probability space ([REJ] "Background", top-k step (b)). Probabilities are the
+  weights over Z, so the midpoint is taken on the weights: w1 = (w_c + w_hi) / 2 in binary64,
+  with w_hi = 1 (the maximum's weight) at the start; "entries greater than the pivot" are the
+  tokens with w > w1. When the support lies between the two pivots the upper bound becomes
+  w1; when it lies above the second pivot the bound stays.
 * Random words. Round j draws the 32-bit word 0 of Philox4x32-10 with key (seed lo, seed
   hi) and counter (j, row, 1, 0) (the Gumbel stream uses counter word 2 = 0); the CDF
   target is t = floor(word * Q / 2^32) for the current eligible mass Q, and the candidate
@@ -39,8 +42,10 @@ Readings where the page leaves a step open (listed with their reasons in the des
   support (word of counter (max_rounds, row, 1, 0)); ``rounds`` reports -1 then.
 
 Ambiguity: the GPU's weights carry about 1.6e-7 relative error. A row is flagged
-``ambiguous`` when a CDF crossing, a top-p comparison or a min-p test lies within that
-error of flipping; such rows are checked for validity only.
+``ambiguous`` when a CDF crossing, a top-p comparison, a min-p test or a token's weight
+against the second pivot lies within that error of flipping; such rows are checked for
+validity only. ``support_exact`` says whether the support's size itself is beyond doubt
+(its boundary is set by k, or the top-p and min-p tests at the boundary are not close).
 """
 from __future__ import annotations
 
@@ -57,6 +62,7 @@ from .sampler import (STATUS_BAD_MINP, STATUS_OK, logits_status, params_status, 
 
 REL_ERR = 5e-7          # margin for the GPU's weight error (about 1.6e-7) plus rounding
 MINP_REL = 1e-6         # min-p tests this close to a weight are flagged
+PIVOT_REL = 1e-6        # weights this close to the second pivot are flagged
 MAX_ROUNDS_LIMIT = 64
 
 
@@ -67,6 +73,7 @@ class RejectionResult:
     rounds: int = 0            # accepted at this round (1-based); 0 greedy/rejected row; -1 fallback
     ambiguous: bool = False
     support_n: int = 0         # n_S by the definition
+    support_exact: bool = True  # n_S is not within the weight error of a top-p / min-p flip
     order: Optional[np.ndarray] = None   # canonical order of the row
 
 
@@ -152,33 +159,49 @@ def rejection_sample_row(row, k: Optional[int], p: Optional[float], t: Optional[
         return topp_on and abs(mass - target) <= REL_ERR * Z + 2 * V + 2
 
     eligible = ok.copy()
-    hi = np.float32(m)
+    hi = 1.0                                    # upper bound: the maximum's weight
     for j in range(max_rounds):
         c = draw(eligible, word_of(j))
-        x0 = np.float32(x[c])
-        x1 = np.float32(np.float32(0.5) * x0) + np.float32(np.float32(0.5) * hi)
+        w1 = 0.5 * float(w[c]) + 0.5 * hi        # second pivot, halfway in probability
         above0 = _above(x, ids, c)
         n0 = int(above0.sum())
         mass0 = int(M[above0].sum())
-        above1 = x > float(x1)
+        above1 = w > w1
         n1 = int(above1.sum())
         mass1 = int(M[above1].sum())
         if near_target(mass0) or near_target(mass1):
             res.ambiguous = True
+        # A weight within the GPU's error of the pivot could land on the other side. Weights
+        # of 1 (the maximum and its ties) are exact on both sides, and so is the pivot 1
+        # (candidate of weight 1, bound 1), which no weight exceeds.
+        if not (float(w[c]) == 1.0 and hi == 1.0):
+            near = (np.abs(w - w1) <= PIVOT_REL * w1) & (w != 1.0)
+            if bool(near.any()):
+                res.ambiguous = True
         if n0 < ke and (not topp_on or mass0 < target):
             res.token = c
             res.rounds = j + 1
-            return res
+            break
         if n1 >= ke or (topp_on and mass1 >= target):
             eligible = above1 & ok              # the support lies above the second pivot
         else:
             eligible = above0 & ok              # the support lies above the candidate
-            hi = x1
+            hi = w1
+    else:
+        res.rounds = -1
+    # Is the support's size beyond the GPU's weight error? (It is exact when k sets it.)
+    if n_s < ke:
+        if topp_on and n_p == n_s:
+            before = int(prefix[n_p - 2]) if n_p >= 2 else 0
+            if near_target(int(prefix[n_p - 1])) or near_target(before):
+                res.support_exact = False
+        if mp > 0.0 and n_m == n_s and bool(near_minp.any()):
+            res.support_exact = False
+    if res.rounds != -1:
+        return res
     # Cap reached: one exact draw over the support ([REJ] "Task" item 2).
-    if topp_on:
-        before = int(prefix[n_p - 2]) if n_p >= 2 else 0
-        if near_target(int(prefix[n_p - 1])) or near_target(before):
-            res.ambiguous = True
+    if not res.support_exact:
+        res.ambiguous = True
     support = np.zeros(V, dtype=bool)
     support[order[:n_s]] = True
     res.token = draw(support, word_of(max_rounds))

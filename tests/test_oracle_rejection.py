@@ -193,24 +193,54 @@ def test_near_uniform_long_row_converges():
 
 
 def test_worked_trajectory_with_injected_words():
-    # x = 0..15, T = 1, k = 4, worked by hand from the page's rule. Round 0 draws token 9:
-    # 6 tokens rank above it (reject); the second pivot (9 + 15) / 2 = 12 has 3 above it
-    # (< k), so the support lies above the candidate: eligible {10..15}, upper bound 12.
-    # Round 1, word 0: the first eligible token, 10: 5 above (reject); pivot (10 + 12) / 2
-    # = 11 has 4 above (>= k): eligible {12..15}. Round 2, word 0: token 12, 3 above:
-    # accepted at round 3.
+    # x = 0..15, T = 1, k = 4, weights w_i = e^(i - 15), worked by hand from the page's rule
+    # (second pivot halfway between the candidate's probability and the upper bound, which
+    # starts at the maximum's weight 1). Round 0 draws token 9: 6 tokens rank above it
+    # (reject); pivot (e^-6 + 1) / 2 = 0.5012 has only token 15 above it (< k), so the support
+    # lies above the candidate: eligible {10..15}, upper bound 0.5012. Round 1, word 0: the
+    # first eligible token, 10: 5 above (reject); pivot (e^-5 + 0.5012) / 2 = 0.2540 has 2
+    # above (15, 14): eligible {11..15}, bound 0.2540. Round 2: token 11, 4 above (reject);
+    # pivot (e^-4 + 0.2540) / 2 = 0.1362 still has 2 above (e^-2 = 0.1353 is below it):
+    # eligible {12..15}. Round 3: token 12, 3 above: accepted at round 4. (A midpoint taken
+    # on logits, (9 + 15) / 2 = 12, would have accepted at round 3.)
     x = np.arange(16, dtype=np.float32)
     e = [math.exp(i - 15) for i in range(16)]
     w0 = int((sum(e[:9]) + 0.5 * e[9]) / sum(e) * 2 ** 32)
     r = rejection_sample_row(x, 4, 1.0, 1.0, 0.0, 0, 0, words=lambda j: w0 if j == 0 else 0)
+    assert (r.token, r.rounds, r.ambiguous) == (12, 4, False)
+    # The other branch: T = 10, weights e^((i - 15) / 10), words all 0 (each round draws the
+    # lowest eligible id). Round 0: token 0 (weight e^-1.5 = 0.2231), 15 above (reject);
+    # pivot (0.2231 + 1) / 2 = 0.6116 has 5 above it (15..11; e^-0.5 = 0.6065 is below), >= k,
+    # so the support lies above the second pivot: eligible {11..15}, the bound stays 1.
+    # Round 1: token 11, 4 above (reject); pivot (e^-0.4 + 1) / 2 = 0.8352 has 2 above
+    # (15, 14): eligible {12..15}, bound 0.8352. Round 2: token 12, 3 above: accepted.
+    r = rejection_sample_row(x, 4, 1.0, F32(10.0), 0.0, 0, 0, words=lambda j: 0)
     assert (r.token, r.rounds, r.ambiguous) == (12, 3, False)
-    # Top-p form of the same walk: p such that the target lies between the masses of
+    # Top-p form of the T = 1 walk: p such that the target lies between the masses of
     # {12..15} and {11..15}: the support is {11..15} (5 tokens); round 0 draws 9 (rejected:
-    # mass above it exceeds the target), pivot 12 has mass below the target, so eligible
-    # {10..15}; word 0 draws 10 (mass above it reaches the target: rejected); pivot 11 has
-    # mass below the target: eligible {11..15}; word 0 draws 11, whose mass above is below
-    # the target: accepted.
+    # mass above it exceeds the target), pivot 0.5012 has only token 15 above it, whose mass
+    # is below the target, so eligible {10..15}, bound 0.5012; word 0 draws 10 (mass above
+    # it reaches the target: rejected); pivot 0.2540 has {15, 14} above it, mass below the
+    # target: eligible {11..15}; word 0 draws 11, whose mass above is below the target:
+    # accepted at round 3.
     above = lambda n: sum(e[16 - n:]) / sum(e)          # mass of the top n tokens
     p = F32(0.5 * (above(4) + above(5)))
     r = rejection_sample_row(x, None, p, 1.0, 0.0, 0, 0, words=lambda j: w0 if j == 0 else 0)
-    assert (r.token, r.rounds, r.support_n) == (11, 3, 5)
+    assert (r.token, r.rounds, r.support_n, r.support_exact) == (11, 3, 5, True)
+
+
+def test_pivot_ties_flag_the_row():
+    # Weights 1, 0.6, 0.2, 0.2 with k = 2: the injected word draws token 2 (mid-way through
+    # its mass); the second pivot (0.2 + 1) / 2 = 0.6 equals token 1's weight, which a GPU
+    # weight 1.6e-7 off could put on either side, so the row is flagged (validity only). With
+    # 0.59 in place of 0.6 the pivot is clear of every weight and the row is not flagged.
+    def run(w1):
+        x = np.log(np.array([1.0, w1, 0.2, 0.2])).astype(np.float32)
+        w = np.exp(x.astype(np.float64) - float(x.max()))
+        M = np.floor(np.ldexp(w, 63 - 3))
+        word = int((M[0] + M[1] + 0.5 * M[2]) / M.sum() * 2 ** 32)
+        return rejection_sample_row(x, 2, 1.0, 1.0, 0.0, 0, 0, words=lambda j: word if j == 0 else 0)
+    r = run(0.6)
+    assert r.ambiguous and r.token in (0, 1)
+    r = run(0.59)
+    assert not r.ambiguous and r.token in (0, 1)

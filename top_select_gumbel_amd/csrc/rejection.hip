@@ -22,8 +22,11 @@
 //   round j   wave 0 finds the tile where the running eligible mass first exceeds
 //             t = floor(word_j * Q / 2^32), then the token inside it: the candidate c. One
 //             counting pass then gives the count and mass of the tokens ranked above c and of
-//             those above the second pivot x1, with per-tile masses of both sets, so the next
-//             round's CDF scan reads one tile only;
+//             those above the second pivot, with per-tile masses of both sets, so the next
+//             round's CDF scan reads one tile only. The second pivot lies halfway between
+//             the candidate's probability and the interval's upper bound (which starts at
+//             the maximum's), i.e. at the weight w1 = (w_c + w_hi) / 2; the tokens above it
+//             are those whose key reaches K1, the smallest key with weight above w1;
 //   fallback  after max_rounds rejections: bisection over the (key, id) order, one counting
 //             pass per step (at most 64), finds the support's last token; one CDF draw over
 //             the support follows.
@@ -333,6 +336,21 @@ __device__ __forceinline__ void cdf_draw(const RowIn& R, const JParams& P, const
   }
 }
 
+// The smallest key whose weight exceeds w1 (> 0), or kmax + 1 when none does: the tokens
+// "greater than" the second pivot are then exactly those with key >= K1, a prefix of the row
+// order whatever the rounding of the weights. Bisection over [key(-inf), kmax]; every key in
+// that range decodes to a finite fp32 value <= the row maximum. Uniform over the workgroup.
+__device__ __forceinline__ uint32_t first_key_above(float w1, uint32_t kmax, const Weigh& W) {
+  if (!(weight32(kmax, W.m, W.c2) > w1)) return kmax + 1u;
+  uint32_t lo = kKeyNegInf, hi = kmax;   // weight(lo) = 0 <= w1 < weight(hi)
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (weight32(mid, W.m, W.c2) > w1) hi = mid;
+    else lo = mid;
+  }
+  return hi;
+}
+
 __device__ __forceinline__ uint64_t draw_target(uint64_t seed, int r, int j, uint64_t q) {
   const uint32_t word = philox4x32_10((uint32_t)j, (uint32_t)r, (uint32_t)seed, (uint32_t)(seed >> 32), 1u).x;
   return (uint64_t)(((unsigned __int128)word * q) >> 32);
@@ -449,7 +467,8 @@ __global__ void __launch_bounds__(kJT) ts_rejection_kernel(JParams P) {
 
   // Rejection rounds.
   Thr E = kThrAll;
-  float hi = W.m;
+  float hi = 1.0f;   // the interval's upper bound, as a weight: the maximum's
+
   int32_t token = -1, rounds = -1;
   for (int j = 0; j < P.max_rounds; ++j) {
     if (wave() == 0) cdf_draw(R, P, W, E, sm.ts[cur], draw_target(seed, r, j, Q), sm);
@@ -460,24 +479,26 @@ __global__ void __launch_bounds__(kJT) ts_rejection_kernel(JParams P) {
     }
     bar();
     const uint32_t c = uni(sm.cand[0]), kc = uni(sm.cand[1]);
-    const float x0 = key2f(kc);
-    const float x1 = __fadd_rn(__fmul_rn(0.5f, x0), __fmul_rn(0.5f, hi));
-    const Thr A{kc, c}, B{f2key(x1), 0u};
+    // second pivot: halfway between the candidate's weight and the upper bound ([REJ]
+    // "Background", top-k step (b), in probability space: probabilities are weights / Z)
+    const float wc = weight32(kc, W.m, W.c2);
+    const float w1 = __fadd_rn(__fmul_rn(0.5f, wc), __fmul_rn(0.5f, hi));
+    const Thr A{kc, c}, B{first_key_above(w1, kmax, W), 0xFFFFFFFFu};   // B: key >= K1
     const Counts n = count_pass<true>(R, P, W, A, B, sm.ts[iA], sm.ts[iB], sm);
     if (n.nA < ke && (!topp_on || n.mA < target)) {
       token = (int32_t)c;
       rounds = j + 1;
       break;
     }
-    if (n.nB >= ke || (topp_on && n.mB >= target)) {   // the support lies above x1
+    if (n.nB >= ke || (topp_on && n.mB >= target)) {   // the support lies above the second pivot
       E = B;
       Q = n.qB;
       cur = iB;
-    } else {                                            // above the candidate, below x1
+    } else {                                            // above the candidate, below the pivot
       E = A;
       Q = n.qA;
       cur = iA;
-      hi = x1;
+      hi = w1;
     }
   }
 
