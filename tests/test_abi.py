@@ -1,22 +1,26 @@
 """Host-side checks of the C ABI that need no GPU: the library loads, exports every symbol
-include/topselect.h declares, sizes workspaces, and rejects bad arguments before touching a
+include/*.h declares, sizes workspaces, and rejects bad arguments before touching a
 device (no compute calls are made here)."""
 import ctypes
+import glob
 import os
 import re
+import threading
 
 import pytest
 
 import top_select_gumbel_amd as ts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "topselect.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ts_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(ts_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -92,6 +96,25 @@ def test_status_strings_and_knobs(lib):
     big = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
     assert small != big
     assert lib.ts_debug_set(99, 1) == -1
+
+
+def test_knobs_belong_to_the_calling_thread(lib):
+    # a chunk size forced on another thread changes neither this thread's setting nor the
+    # workspace size it computes
+    base = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
+    seen = {}
+
+    def other():
+        seen["old"] = lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 1024)
+        seen["ws"] = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
+        seen["main_during"] = None
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["old"] == 0 and seen["ws"] != base
+    assert lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0) == base
+    assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0) == 0          # this thread never changed
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -1,14 +1,19 @@
 """GPU parity of the three C-ABI entry points against the binary64 oracle.
 
-Sizes span several workgroup chunks and ragged tails; the full-size workloads are checked
-on sampled rows. Every case prints a [case] line first so a failure can be located.
+Sizes span several workgroup chunks and ragged tails; the full-size workloads (decode
+64 x 151936, tie stress 128 x 128256, indexer 32 x 131072) are checked on every row, the
+oracle side running row-parallel in a process pool (oracle_pool). Every case prints a
+[case] line first so a failure can be located.
 """
+import math
+
 import numpy as np
 import pytest
 
 import oracle
 import top_select_gumbel_amd as ts
 from top_select_gumbel_amd import workloads as wl
+import oracle_pool as op
 from gpu_helpers import banner, check_samples, check_topk, check_topp, dev, host, torch_cuda
 
 pytestmark = pytest.mark.gpu
@@ -103,16 +108,24 @@ def test_noise_transform_over_every_magnitude_of_u():
 
 
 def test_noise_clamp_endpoints():
-    banner("gumbel noise: clamp end points")
-    # find tokens whose words are extreme is impractical; check the map through the debug
-    # kernel on tokens and compare the formula at the two clamp ends via the oracle instead
+    # The two ends of the clamp in closed form: word 0 maps to u = 0, clamped up to 2^-32,
+    # so g = -log(-log1p(-2^-32)) = -log(2^-32 + 2^-65 + ...) = 32 ln 2 - ... ~ 22.18; the
+    # largest word rounds to u = 1, clamped down to 1 - 2^-24, so g = -log(24 ln 2) ~ -2.81.
+    # Words next to them stay inside the clamp.
+    banner("gumbel noise: clamp end points in closed form")
     torch = torch_cuda()
-    toks = np.arange(0, 1 << 16, dtype=np.int32)
-    w, u, g = ts.ts_gumbel_noise(123, 4, dev(toks))
+    words = np.array([0, 1, 2, 0xFFFFFFFF, 0xFFFFFF80, 0xFFFFFF7F], dtype=np.uint64).astype(np.uint32)
+    u, g = ts.ts_noise_transform(dev(words.view(np.int32)))
     torch.cuda.synchronize()
-    u = host(u)
-    assert u.min() >= 2.0 ** -32 and u.max() <= 1 - 2.0 ** -24
-    assert np.isfinite(host(g)).all()
+    u, g = host(u).astype(np.float64), host(g).astype(np.float64)
+    lo, hi = 2.0 ** -32, 1.0 - 2.0 ** -24
+    assert u[0] == lo and u[1] == lo and u[2] == 2.0 ** -31
+    assert u[3] == hi and u[4] == hi and u[5] == hi
+    g_lo = -math.log(-math.log1p(-lo))
+    g_hi = -math.log(-math.log1p(-hi))
+    assert abs(g_lo - 32 * math.log(2)) < 1e-8 and abs(g_hi + math.log(24 * math.log(2))) < 1e-6
+    ref = np.array([g_lo, g_lo, -math.log(-math.log1p(-2.0 ** -31)), g_hi, g_hi, g_hi])
+    assert np.all(np.abs(g - ref) <= g_tol(ref)), (g, ref)
 
 
 # ----------------------------------------------------------------------------- top-k
@@ -171,12 +184,11 @@ def test_topk_large_k_stream_path():
     check_topk(b.logits, b.k, 6000, out, st, "large-k")
 
 
-def test_topk_indexer_rows_sampled():
+def test_topk_indexer_rows_every_row():
     b = wl.indexer_rows()
-    banner("topk indexer 32x131072 k=2048 (8 rows checked)")
+    banner("topk indexer 32x131072 k=2048 (every row)")
     out, st = run_topk(b.logits, b.k, 2048)
-    sel = [0, 3, 8, 13, 21, 26, 30, 31]
-    check_topk(b.logits[sel], b.k[sel], 2048, out[sel], st[sel], "indexer")
+    op.check_topk(b.logits, b.k, 2048, out, st, "indexer")
 
 
 def test_topk_indexer_long_and_near_uniform():
@@ -279,33 +291,42 @@ def test_topp_topk_off_and_special():
     check_topp(x, k, p, t, kept, mask, st, "k-mixed")
 
 
-def test_topp_decode_rows_sampled():
+def test_topp_decode_every_row():
     b = wl.decode()
-    banner("topp decode 64x151936 (16 rows checked)")
+    banner("topp decode 64x151936 (every row, masks)")
     kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
-    sel = list(range(0, 64, 4))
-    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "decode")
+    op.check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "decode")
 
 
-def test_topp_and_sample_decode_topk_off_sampled():
-    # top-p over whole 151936-element rows (top-k disabled): the row-streaming path with its
-    # boundary bin continued in LDS and the Gumbel draws compacted to the kept set
-    b = wl.decode_topp_only()
-    banner("topp + sample decode with k off 64x151936 (8 rows checked)")
+def test_topp_and_sample_decode_topk_off_every_row():
+    # top-p over whole 151936-element rows (top-k disabled): the nucleus passes, or with a
+    # top-k array of k = V the per-row path
+    b = wl.decode_topp_only()                 # a top-k array holding k = V
+    banner("topp + sample decode with k off 64x151936 (every row)")
     kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
     tok, st2 = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
-    sel = [0, 2, 11, 16, 33, 47, 56, 59]
-    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "topk-off")
-    check_samples(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], b.seeds[sel], tok[sel], st2[sel], kept[sel],
-                  "topk-off", row_ids=sel)
+    op.check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "topk-off")
+    op.check_samples(b.logits, b.k, b.p, b.t, b.seeds, tok, st2, kept, "topk-off")
+    # no top-k array at all: the same bytes
+    kept2, mask2, st3 = run_topp(b.logits, None, b.p, b.t, want_mask=True)
+    tok2, _ = run_sample(b.logits, None, b.p, b.t, b.seeds)
+    assert np.array_equal(kept2, kept) and np.array_equal(mask2, mask) and np.array_equal(st3, st)
+    assert np.array_equal(tok2, tok)
 
 
-def test_topp_tie_stress_sampled():
+def test_tie_stress_every_row():
+    # bf16-rounded logits at 1e5 scale (exact ties everywhere) and one all-equal row (the
+    # last): top-k bytes, top-p counts and masks, and sampled ids on all 128 rows
     b = wl.tie_stress()
-    banner("topp tie stress 128x128256 (12 rows incl. the all-equal row)")
+    banner("tie stress 128x128256: topk + topp + sample (every row, incl. the all-equal row)")
+    out, st0 = run_topk(b.logits, b.k, 2048)
+    op.check_topk(b.logits, b.k, 2048, out, st0, "tie topk")
+    assert out[127, : b.k[127]].tolist() == list(range(b.k[127]))      # all equal: ids [0, k)
     kept, mask, st = run_topp(b.logits, b.k, b.p, b.t, want_mask=True)
-    sel = list(range(0, 128, 12)) + [127]
-    check_topp(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], kept[sel], mask[sel], st[sel], "tie")
+    op.check_topp(b.logits, b.k, b.p, b.t, kept, mask, st, "tie topp")
+    tok, st2 = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
+    exempt = op.check_samples(b.logits, b.k, b.p, b.t, b.seeds, tok, st2, kept, "tie sample")
+    assert exempt <= 4
 
 
 # ----------------------------------------------------------------------------- sampling
@@ -337,14 +358,12 @@ def test_sample_random_and_paths():
     check_samples(x, k, p, t, seeds, tok, st, kept, "mixed")
 
 
-def test_sample_decode_rows_sampled():
+def test_sample_decode_every_row():
     b = wl.decode()
-    banner("sample decode 64x151936 (16 rows checked)")
+    banner("sample decode 64x151936 (every row)")
     tok, st = run_sample(b.logits, b.k, b.p, b.t, b.seeds)
     kept, _, _ = run_topp(b.logits, b.k, b.p, b.t, want_mask=False)
-    sel = list(range(1, 64, 4))
-    res, exempt = check_samples(b.logits[sel], b.k[sel], b.p[sel], b.t[sel], b.seeds[sel], tok[sel], st[sel],
-                                kept[sel], "decode", row_ids=sel)
+    exempt = op.check_samples(b.logits, b.k, b.p, b.t, b.seeds, tok, st, kept, "decode")
     assert exempt <= 2
 
 

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_pool as op
 import top_select_gumbel_amd as ts
 from top_select_gumbel_amd import workloads as wl
 from gpu_helpers import banner, dev, host, torch_cuda
@@ -70,8 +71,12 @@ def test_indexer_rows_ragged_transform():
     rng = np.random.default_rng(73)
     lengths = rng.integers(1000, 131072 + 1, 32).astype(np.int32)
     offsets = (np.arange(32) * 131072 % (1 << 30)).astype(np.int32)   # each row's start in a flat space
-    banner("topk rows indexer 32x131072 k=2048, value order, ragged offsets (8 rows checked)")
-    check(b.logits, b.k, 2048, lengths, ts.TS_ORDER_VALUE, offsets, "indexer", rows=[0, 5, 9, 14, 18, 23, 27, 31])
+    banner("topk rows indexer 32x131072 k=2048, value order, ragged offsets (every row)")
+    out, st = run(b.logits, b.k, 2048, lengths, ts.TS_ORDER_VALUE, offsets)
+    args = [("indexer", r, b.logits[r], int(lengths[r]), int(b.k[r]), 2048, ts.TS_ORDER_VALUE, int(offsets[r]),
+             out[r], int(st[r])) for r in range(32)]
+    errs = [e for e in op.pool().map(op.topk_rows_row, args, chunksize=1) if e]
+    assert not errs, "; ".join(errs[:4])
 
 
 def test_null_lengths_match_plain_topk():

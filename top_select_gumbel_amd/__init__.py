@@ -4,7 +4,8 @@ Argument marshalling only: every step of the sampling path runs in the HIP libra
 functions take torch tensors that already live on the GPU and enqueue on the current torch
 stream. There is no CPU fallback: if the library is missing, calls raise.
 
-Names mirror the C ABI in include/topselect.h.
+Names mirror the C ABI in include/topselect.h (ts_debug_set: the test hooks of
+include/topselect_testing.h).
 """
 from __future__ import annotations
 

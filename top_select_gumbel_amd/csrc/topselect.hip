@@ -55,6 +55,7 @@
 #include <vector>
 
 #include "topselect.h"
+#include "topselect_testing.h"
 #include "ts_device.hpp"
 #include "ts_host.hpp"
 
@@ -2799,9 +2800,11 @@ namespace {
 using tsh::check_device;
 using tsh::fail;
 
-std::atomic<int64_t> g_knob_chunk{0};
-std::atomic<int64_t> g_knob_exact{0};
-std::atomic<int64_t> g_knob_direct{1};
+// Test hooks (topselect_testing.h): per calling thread, so that a setting made by one thread
+// never reaches another thread's calls or workspace sizes.
+thread_local int64_t g_knob_chunk = 0;
+thread_local int64_t g_knob_exact = 0;
+thread_local int64_t g_knob_direct = 1;
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
@@ -2815,7 +2818,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // (the wave's exponential sum, used by sampling with logprobs).
 bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   if (rows < 0 || V < 1 || V > TS_MAX_VOCAB) return false;
-  int64_t ce = g_knob_chunk.load();
+  int64_t ce = g_knob_chunk;
   if (ce <= 0) ce = kChunkMax;
   const int64_t chunks0 = (V + ce - 1) / ce;
   int64_t len = (V + chunks0 - 1) / chunks0;
@@ -2881,9 +2884,9 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.chunk_len = (int32_t)pl.chunk_len;
   P.cap_w = (int32_t)pl.cap_w;
   P.xcd_map = (pl.chunks > 1 && rows % 8 == 0) ? 1 : 0;
-  P.force_exact = (int32_t)g_knob_exact.load();
+  P.force_exact = (int32_t)g_knob_exact;
   // Rows that fit the row kernel's LDS skip the stream kernel (unless a chunk size is forced).
-  P.direct = (V <= kLdsCand && g_knob_chunk.load() == 0 && g_knob_direct.load() != 0) ? 1 : 0;
+  P.direct = (V <= kLdsCand && g_knob_chunk == 0 && g_knob_direct != 0) ? 1 : 0;
   // No top-k array: every row has top-k off, so rows with top-p or min-p on take the
   // nucleus pass (spread over the chunk workgroups) instead of one workgroup streaming the row.
   P.nucleus = (MODE != kModeTopk && !P.direct && !P.force_exact && k == nullptr && (p != nullptr || minp != nullptr)) ? 1 : 0;
@@ -3062,10 +3065,20 @@ int64_t ts_debug_set(int knob, int64_t value) {
   switch (knob) {
     case TS_KNOB_CHUNK_ELEMS: {
       if (value != 0 && (value < 64 || value > kChunkMax || value % 64 != 0)) return -1;
-      return g_knob_chunk.exchange(value);
+      const int64_t old = g_knob_chunk;
+      g_knob_chunk = value;
+      return old;
     }
-    case TS_KNOB_FORCE_EXACT: return g_knob_exact.exchange(value ? 1 : 0);
-    case TS_KNOB_DIRECT: return g_knob_direct.exchange(value ? 1 : 0);
+    case TS_KNOB_FORCE_EXACT: {
+      const int64_t old = g_knob_exact;
+      g_knob_exact = value ? 1 : 0;
+      return old;
+    }
+    case TS_KNOB_DIRECT: {
+      const int64_t old = g_knob_direct;
+      g_knob_direct = value ? 1 : 0;
+      return old;
+    }
     default: return -1;
   }
 }
