@@ -168,6 +168,24 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ts_sample_rows_noalloc -- ts_sample_rows for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments and the
+ * same results (byte for byte) as ts_sample_rows, without the workspace: the library keeps it
+ * in a static device array of 16 MiB per GPU (held from the library's load until the process
+ * ends), found once per device with hipGetSymbolAddress. The call allocates nothing. Its
+ * candidate slices hold 256 candidates per wave; rows whose waves publish more (massive ties)
+ * take the exact path, which gives the same bytes at a higher cost.
+ * Limit: the batch must fit the scratch (about 8.4 KB per 8192-logit chunk of a row plus
+ * 8.3 KB per row: the 64 x 151936 decode batch takes 11 MB); larger batches fail with
+ * TS_ERR_INVALID_ARG and a message in ts_last_error, before any device work.
+ * Calls that overlap on one GPU (other streams, other threads) share the one array and race;
+ * serialise them. Nothing in the array needs to start at zero.
+ */
+int ts_sample_rows_noalloc(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                           const int32_t* top_k, const float* top_p, const float* temperature,
+                           const uint64_t* seed, int32_t* out_token, int32_t* row_status, void* stream);
+
+/*
  * ts_sample_rows_logp -- ts_sample_rows plus the sampled token's log-probability under the
  * row's temperature-scaled distribution, [LOGP] "Design: the numeric contract" with
  * temperature applied in the epilogue ([LOGP] "Contract constants"): over the WHOLE row

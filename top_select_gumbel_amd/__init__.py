@@ -39,7 +39,7 @@ TS_KNOB_DIRECT = 3
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",
-    "ts_sample_rows", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_noise_transform", "ts_read_ceiling", "ts_debug_set", "ts_status_string", "ts_last_error",
+    "ts_sample_rows", "ts_sample_rows_noalloc", "ts_sample_rows_logp", "ts_topp_mask_minp", "ts_sample_rows_minp", "ts_sample_rows_rejection", "ts_gumbel_noise", "ts_noise_transform", "ts_read_ceiling", "ts_debug_set", "ts_status_string", "ts_last_error",
 )
 
 _lib = None
@@ -76,6 +76,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         lib.ts_topp_mask.restype = c.c_int
         lib.ts_sample_rows.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_sample_rows.restype = c.c_int
+        lib.ts_sample_rows_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        lib.ts_sample_rows_noalloc.restype = c.c_int
         lib.ts_sample_rows_logp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ts_sample_rows_logp.restype = c.c_int
         lib.ts_topp_mask_minp.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -227,6 +229,24 @@ def ts_sample_rows(logits, top_k, top_p, temperature, seed, out_token=None, stat
     _check(lib.ts_sample_rows(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
                               _ptr(temperature), _ptr(seed), _ptr(tok), _ptr(st), _ptr(ws),
                               ws.numel(), _stream()))
+    return tok, st
+
+
+def ts_sample_rows_noalloc(logits, top_k, top_p, temperature, seed, out_token=None, status=None):
+    """ts_sample_rows without a workspace (the library's static scratch): same results.
+    Allocates only the output tensors when they are not given."""
+    import torch
+    lib = load_library()
+    rows, v, stride = _rows_view(logits)
+    top_k = _opt(top_k, "torch.int32", rows)
+    top_p = _opt(top_p, "torch.float32", rows)
+    temperature = _opt(temperature, "torch.float32", rows)
+    if seed is None or str(seed.dtype) not in ("torch.uint64", "torch.int64") or seed.numel() != rows:
+        raise TopSelectError("seed must be a uint64/int64 device tensor with one entry per row")
+    tok = out_token if out_token is not None else torch.empty(rows, dtype=torch.int32, device=logits.device)
+    st = status if status is not None else torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _check(lib.ts_sample_rows_noalloc(_ptr(logits), rows, v, stride, _ptr(top_k), _ptr(top_p),
+                                      _ptr(temperature), _ptr(seed), _ptr(tok), _ptr(st), _stream()))
     return tok, st
 
 

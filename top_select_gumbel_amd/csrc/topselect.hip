@@ -2224,7 +2224,10 @@ __device__ __forceinline__ bool nucleus_finish(const Params& P, const RowPlan& r
     const uint32_t n_above = n_up;   // counted by the cut pass for the same cut bin
     ncut = n_list;
     const uint64_t ma = sm.res64[0];
-    if (ncut > (uint32_t)kLdsCand) return false;
+    // the cut pass listed at most this many (the LDS, and the row's candidate slices); a
+    // longer cut bin was not stored whole and the row takes the row-streaming path
+    const uint32_t cap_list = (uint32_t)min((int64_t)kLdsCand, (int64_t)nseg * P.cap_w);
+    if (ncut > cap_list) return false;
     const uint2* list = P.cand + (int64_t)r * nseg * P.cap_w;   // ncut entries, any order
     for (uint32_t i0 = threadIdx.x; i0 < ncut; i0 += 8 * kRT) {
       uint2 e[8];
@@ -2816,7 +2819,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Chunking of a row and the workspace layout: per (row, chunk, wave) a WaveInfo, then per
 // (row, chunk, wave) a slice of cap_w candidate slots, then per (row, chunk, wave) one double
 // (the wave's exponential sum, used by sampling with logprobs).
-bool make_plan(int64_t rows, int64_t V, Plan& pl) {
+bool make_plan(int64_t rows, int64_t V, Plan& pl, int64_t cap_limit = kCapW) {
   if (rows < 0 || V < 1 || V > TS_MAX_VOCAB) return false;
   int64_t ce = g_knob_chunk;
   if (ce <= 0) ce = kChunkMax;
@@ -2826,7 +2829,7 @@ bool make_plan(int64_t rows, int64_t V, Plan& pl) {
   pl.chunk_len = len;
   pl.chunks = (V + len - 1) / len;
   const int64_t qw = ((len + 3) / 4 + kW1 - 1) / kW1;   // quads per wave
-  pl.cap_w = 4 * qw < kCapW ? 4 * qw : kCapW;
+  pl.cap_w = 4 * qw < cap_limit ? 4 * qw : cap_limit;
   const int64_t rr = rows > 0 ? rows : 1;
   if (rr * pl.chunks * kW1 > (int64_t)0x7FFFFFFF) return false;
   const size_t nseg = (size_t)(rr * pl.chunks * kW1);
@@ -2849,7 +2852,7 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
            uint8_t* out_mask, int32_t* out_token, int32_t* status, void* ws, size_t ws_bytes,
            void* stream, float* out_logp = nullptr, float* out_lse = nullptr,
            const float* minp = nullptr, const int32_t* lengths = nullptr, const int32_t* offsets = nullptr,
-           int order = TS_ORDER_INDEX) {
+           int order = TS_ORDER_INDEX, int64_t cap_limit = kCapW) {
   if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
   if (V < 1 || V > TS_MAX_VOCAB) return fail(TS_ERR_INVALID_ARG, "vocab = %lld outside [1, 2^30]", (long long)V);
   if (stride < V) return fail(TS_ERR_INVALID_ARG, "row_stride %lld < vocab %lld", (long long)stride, (long long)V);
@@ -2857,7 +2860,7 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   if (!x) return fail(TS_ERR_INVALID_ARG, "logits pointer is NULL");
   if (rows > 0x7FFFFFFF) return fail(TS_ERR_INVALID_ARG, "rows too large");
   Plan pl;
-  if (!make_plan(rows, V, pl)) return fail(TS_ERR_INVALID_ARG, "rows x chunks too large");
+  if (!make_plan(rows, V, pl, cap_limit)) return fail(TS_ERR_INVALID_ARG, "rows x chunks too large");
   if (!ws) return fail(TS_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)ws & 255u) != 0) return fail(TS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (ws_bytes < pl.total)
@@ -2923,6 +2926,34 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
     hipLaunchKernelGGL((ts_row_kernel<MODE, false>), dim3((unsigned)rows), dim3(kRT), 0, s, P);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "row kernel launch failed: %s", hipGetErrorString(e));
+  return TS_OK;
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// ts_sample_rows_noalloc keeps its workspace in this array: one copy per GPU, held until the
+// process ends. Its candidate slices hold at most kCapNoAlloc candidates per wave (a wave with
+// more flags an overflow and its row takes the exact path, which gives the same bytes), so the
+// decode batch (64 x 151936) needs about 11 MB of it.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int64_t kCapNoAlloc = 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on each GPU (the host-side name is only a stand-in):
+// looked up once per device, with that device current.
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(TS_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return TS_OK;
 }
 
@@ -2996,6 +3027,31 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
   return launch<kModeSample>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, seed,
                              nullptr, nullptr, nullptr, out_token, row_status, workspace,
                              workspace_bytes, stream);
+}
+
+int ts_sample_rows_noalloc(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                           const int32_t* top_k, const float* top_p, const float* temperature,
+                           const uint64_t* seed, int32_t* out_token, int32_t* row_status, void* stream) {
+  if (rows > 0 && (!seed || !out_token)) return fail(TS_ERR_INVALID_ARG, "seed and out_token are required");
+  if (rows < 0) return fail(TS_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
+  if (rows == 0) return TS_OK;
+  Plan pl;
+  if (!make_plan(rows, vocab, pl, kCapNoAlloc))
+    return fail(TS_ERR_INVALID_ARG, "vocab = %lld or rows x chunks outside the supported range", (long long)vocab);
+  if (pl.total > kScratchBytes)
+    return fail(TS_ERR_INVALID_ARG,
+                "%lld rows of %lld logits need %zu bytes of scratch; ts_sample_rows_noalloc holds %zu "
+                "(use ts_sample_rows with a workspace)",
+                (long long)rows, (long long)vocab, pl.total, kScratchBytes);
+  int dev;
+  int rc = check_device(&dev);
+  if (rc != TS_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(dev, &ws);
+  if (rc != TS_OK) return rc;
+  return launch<kModeSample>(logits, rows, vocab, row_stride, top_k, 0, top_p, temperature, seed,
+                             nullptr, nullptr, nullptr, out_token, row_status, ws, kScratchBytes, stream,
+                             nullptr, nullptr, nullptr, nullptr, nullptr, TS_ORDER_INDEX, kCapNoAlloc);
 }
 
 int ts_sample_rows_logp(const float* logits, int64_t rows, int64_t vocab, int64_t row_stride,
