@@ -1139,34 +1139,38 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     }
   }
 
-  // From here on every wave works alone. Each slot as it arrives: the quad maximum (one
-  // max3 chain) feeds the wave maximum and the candidate test; unordered compares of element
-  // pairs feed the NaN flag. A quad whose maximum reaches the threshold is staged (values and
-  // quad index) at its ballot rank, which keeps the staged quads in id order.
+  // From here on every wave works alone. Each slot as it arrives: the quad maximum feeds the
+  // wave maximum and the candidate test. It is the IEEE 754-2019 maximum (two v_maximum3),
+  // which propagates NaN, so a lane's running maximum is NaN exactly when one of its elements
+  // was: the NaN flag needs no compares of its own (a row holding a NaN is rejected whatever
+  // its maximum). A quad whose maximum reaches the threshold is staged (values and quad
+  // index) at its ballot rank, which keeps the staged quads in id order; ranks past the
+  // stage's end are clamped onto its last entry, whose contents are then unused (more hits
+  // than the stage holds take the register path below). One loop serves every path (off the
+  // candidate path the test compares against NaN and never hits), so that each slot is
+  // processed as it arrives, with no branch besides the stage write's: every instruction
+  // after the last data arrive is on the critical path.
+  const float stage_thr = cand ? thr_f : __builtin_nanf("");
   float fmx = -INFINITY;
-  bool nan_any = false;
   uint32_t run = 0;
 #pragma unroll
   for (int s = 0; s < kS1; ++s) {
-    const float x0 = xval(s, 0), x1 = xval(s, 1), x2 = xval(s, 2), x3 = xval(s, 3);
-    const float mq = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
-    fmx = fmaxf(fmx, mq);
-    nan_any |= __builtin_isunordered(x0, x1) | __builtin_isunordered(x2, x3);
-    if (cand) {
-      const bool hit = mq >= thr_f;
-      const uint64_t mk = __ballot(hit);
-      if (hit) {
-        const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, run));
-        if (pos < (uint32_t)kQStage) {
-          sm.stage_v[w][pos] = raw[s];
-          sm.stage_q[w][pos] = (uint32_t)(q_lo + s * 64 + l);
-        }
-      }
-      run += (uint32_t)__popcll(mk);
+    const float mq = __builtin_elementwise_maximum(__builtin_elementwise_maximum(xval(s, 0), xval(s, 1)),
+                                                   __builtin_elementwise_maximum(xval(s, 2), xval(s, 3)));
+    fmx = __builtin_elementwise_maximum(fmx, mq);
+    const bool hit = mq >= stage_thr;
+    const uint64_t mk = __ballot(hit);
+    const uint32_t pos = min(__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, run)),
+                             (uint32_t)kQStage - 1u);
+    if (hit) {
+      sm.stage_v[w][pos] = raw[s];
+      sm.stage_q[w][pos] = (uint32_t)(q_lo + s * 64 + l);
     }
+    run += (uint32_t)__popcll(mk);
   }
-  const uint32_t kmax = wave_max(f2key(fmx));
-  uint32_t flags = (__ballot(nan_any) != 0ull) ? kFlagNan : 0u;
+  const bool nan_lane = __builtin_isnan(fmx);
+  const uint32_t kmax = wave_max(f2key(nan_lane ? -INFINITY : fmx));
+  uint32_t flags = (__ballot(nan_lane) != 0ull) ? kFlagNan : 0u;
   const int64_t seg = ((int64_t)r * P.chunks + c) * kW1 + w;
   if (MODE == kModeSample && P.wsum) {
     // [LOGP] "Design: the numeric contract": the wave's share of S = sum exp((x - m) / T),
@@ -1204,34 +1208,38 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     if (run <= (uint32_t)kQStage) {
       wave_lds_sync();
       // Extract the staged quads' elements >= thr in id order: a wave scan of the per-lane
-      // counts gives each lane its first position.
+      // counts gives each lane its first position, and a lane's elements follow in order.
+      // When the wave's slice has room for the whole batch (always, unless the caller capped
+      // the slices) the stores need no bound check.
       for (uint32_t i0 = 0; i0 < run; i0 += 64) {
-        const uint32_t i = i0 + (uint32_t)l;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        uint32_t q = 0xFFFFFFFFu;
-        if (i < run) {
-          v = sm.stage_v[w][i];
-          q = sm.stage_q[w][i];
-        }
+        const uint32_t i = i0 + (uint32_t)l;   // < kQStage: entries at or past run are stale, masked below
+        const uint4 v = sm.stage_v[w][i];
+        const uint32_t q = sm.stage_q[w][i];
         const float y[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
-        const bool qok = i < run && (int)q < q_hi;
+        const int e_lim = (i < run && (int)q < q_hi) ? min(n - 4 * (int)q, 4) : 0;   // valid elements of the quad
+        uint32_t at[4];   // position among the lane's selected elements
         bool sel[4];
         uint32_t cc = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sel[e] = qok && (int)(4 * q) + e < n && y[e] >= thr_f;
+          sel[e] = e < e_lim && y[e] >= thr_f;
+          at[e] = cc;
           cc += sel[e] ? 1u : 0u;
         }
         const uint32_t incl = wave_incl_scan(cc);
-        uint32_t pos = count + incl - cc;
+        const uint32_t pos = count + incl - cc;
+        const uint32_t total = wave_total(incl);
+        const uint32_t id0 = (uint32_t)(c0 + 4 * (int)q);
+        if (count + total <= cap) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (sel[e]) {
-            if (pos < cap) out[pos] = make_uint2(f2key(y[e]), (uint32_t)(c0 + 4 * (int)q + e));
-            ++pos;
-          }
+          for (int e = 0; e < 4; ++e)
+            if (sel[e]) out[pos + at[e]] = make_uint2(f2key(y[e]), id0 + (uint32_t)e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (sel[e] && pos + at[e] < cap) out[pos + at[e]] = make_uint2(f2key(y[e]), id0 + (uint32_t)e);
         }
-        count += wave_total(incl);
+        count += total;
       }
     } else {
       // More hits than the stage holds: the same ordered list, straight from registers.
