@@ -116,3 +116,38 @@ def test_long_rows_flat_gather_all_entry_points():
     tok, st3 = ts.ts_sample_rows(dev(x), dev(k), dev(p), dev(t), dev(seeds))
     torch.cuda.synchronize()
     check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, "long rows")
+
+
+def test_constant_stretches_uniform_slices():
+    """Rows holding stretches of one repeated value (V = 151936: chunks of 8000 logits, wave
+    shares of 2000). A wave whose every element is one key publishes a uniform slice (no
+    stored entries); a wave holding more candidates than its slice flags it overflowed and the
+    row takes the exact path. Both must give the oracle's results in all three entry points."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(5150)
+    rows, v = 6, 151936
+    x = rng.standard_normal((rows, v)).astype(np.float32)
+    x[0, 0:6000] = 9.0                           # three whole wave shares, the row's top
+    x[1, 1000:9000] = 9.0                        # unaligned: partial waves overflow their slices
+    x[2] = np.float32(0.5)                       # all equal
+    x[3, 8000:16000] = 3.0                       # a whole chunk, the top-k boundary inside it
+    x[3, rng.choice(v, 20, replace=False)] += 8.0
+    x[4, 144000:] = 4.0                          # the last chunk, whole and ragged
+    x[5, 50000:58000] = -np.inf                  # a masked chunk below the threshold
+    k = np.array([2048, 1000, 700, 2048, 300, 1024], np.int32)
+    p = np.array([0.9, 0.95, 0.8, 0.99, 0.7, 0.9], np.float32)
+    t = np.array([1.0, 0.7, 1.2, 1.0, 0.0, 1.1], np.float32)
+    seeds = rng.integers(0, 2 ** 64, rows, dtype=np.uint64)
+    banner(f"constant stretches V={v}: topk")
+    idx, st = ts.ts_topk_select(dev(x), dev(k), 2048)
+    torch.cuda.synchronize()
+    check_topk(x, k, 2048, host(idx), host(st), "stretches")
+    banner(f"constant stretches V={v}: topp")
+    kept, mask, st2 = ts.ts_topp_mask(dev(x), dev(k), dev(p), dev(t), True)
+    torch.cuda.synchronize()
+    kept = host(kept)
+    check_topp(x, k, p, t, kept, host(mask), host(st2), "stretches")
+    banner(f"constant stretches V={v}: sample")
+    tok, st3 = ts.ts_sample_rows(dev(x), dev(k), dev(p), dev(t), dev(seeds))
+    torch.cuda.synchronize()
+    check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, "stretches")

@@ -77,10 +77,17 @@ constexpr int kHWords = kHBins + kHBins / 8;        // padded: 4 spare words aft
 constexpr int kH2Bits = 8;                          // second-level digit inside the chosen bin
 constexpr int kH2Bins = 1 << kH2Bits;
 constexpr int kSampleSlots = 2;                     // slots whose keys form the sample
-constexpr int kQStage = 128;                        // staged quads per wave
+constexpr int kQStage = 128;                        // staged quads per wave (a power of two)
+static_assert((kQStage & (kQStage - 1)) == 0, "stage ranks wrap with a mask");
 constexpr int kRefine = 16;                         // sampled keys in a chosen bin that call for a finer level
-constexpr int kCapW = kChunkMax / kW1;              // candidate slots per wave: its whole share, so a
-                                                     // slice cannot overflow (massive ties stay exact)
+constexpr int kCapW = kChunkMax / kW1 / 2;          // candidate slots per wave, at most: half of its
+                                                     // share (less 32), so that the workspace takes no
+                                                     // more bytes than the logits it covers
+constexpr int kCapSmall = 256;                      // waves of at most this many elements keep a slot
+                                                     // for each; larger ones get half their share
+// A wave that finds more candidates than its slice holds flags it overflowed and its row takes
+// the exact path, unless every one of its elements is the same key (a uniform slice, which
+// stores nothing).
 // row kernel
 constexpr int kRT = 512;                            // threads per row workgroup
 constexpr int kRW = kRT / 64;
@@ -107,10 +114,13 @@ struct WaveInfo {
   uint32_t kmax_idx;  // lowest id holding kmax (GREEDY)
   float best_s;       // FULL sampling: best score relative to kmax's value
   int32_t best_idx;
-  uint32_t pad;
+  uint32_t first;     // UNIFORM slices: the id of the wave's first element
 };
 static_assert(sizeof(WaveInfo) == 32, "WaveInfo layout");
-constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u;
+// kFlagUniform: every one of the wave's `count` elements holds the key kmax, so the slice
+// stores no entries: entry j is (kmax, first + j). Only such slices may count past the
+// slice capacity.
+constexpr uint32_t kFlagNan = 1u, kFlagOverflow = 2u, kFlagUniform = 4u;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Per-row state of the nucleus passes. The exact fixed-point mass of every nucleus bin
@@ -183,6 +193,8 @@ struct Smem {
   uint32_t kkey[kFastK];       // the kept set P, compacted for the Gumbel draws
   uint32_t kidx[kFastK];
   uint32_t segoff[kMaxSeg + 1];
+  uint32_t ukey[kMaxSeg];      // per slice: its key when it is uniform, else 0 (no real key is 0)
+  uint32_t ufirst[kMaxSeg];    // per uniform slice: the id of its first entry
   uint32_t red[4 * kRW];
   uint64_t red64[2 * kRW];
   float reds[kRW];
@@ -1145,8 +1157,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   // was: the NaN flag needs no compares of its own (a row holding a NaN is rejected whatever
   // its maximum). A quad whose maximum reaches the threshold is staged (values and quad
   // index) at its ballot rank, which keeps the staged quads in id order; ranks past the
-  // stage's end are clamped onto its last entry, whose contents are then unused (more hits
-  // than the stage holds take the register path below). One loop serves every path (off the
+  // stage's end wrap around it (distinct addresses, no write conflicts), and the stage's
+  // contents are then unused: more hits than it holds take the register path below. One loop serves every path (off the
   // candidate path the test compares against NaN and never hits), so that each slot is
   // processed as it arrives, with no branch besides the stage write's: every instruction
   // after the last data arrive is on the critical path.
@@ -1160,8 +1172,8 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     fmx = __builtin_elementwise_maximum(fmx, mq);
     const bool hit = mq >= stage_thr;
     const uint64_t mk = __ballot(hit);
-    const uint32_t pos = min(__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, run)),
-                             (uint32_t)kQStage - 1u);
+    const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, run)) &
+                         ((uint32_t)kQStage - 1u);
     if (hit) {
       sm.stage_v[w][pos] = raw[s];
       sm.stage_q[w][pos] = (uint32_t)(q_lo + s * 64 + l);
@@ -1242,7 +1254,22 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
         count += total;
       }
     } else {
-      // More hits than the stage holds: the same ordered list, straight from registers.
+      // More hits than the stage holds. When every valid element of the wave is one key
+      // (a constant stretch of the row, e.g. an all-equal row) the slice is uniform and
+      // stores nothing; otherwise the same ordered list, straight from registers.
+      // Every value this wave loaded is an element of the chunk (lanes past the wave's range
+      // hold duplicates), so comparing all of them with the maximum's bits is a test that can
+      // only be stricter than needed (and needs no validity masks).
+      const uint32_t mbits = __float_as_uint(key2f(kmax));
+      uint32_t other = 0u;
+#pragma unroll
+      for (int s = 0; s < kS1; ++s)
+        other |= (raw[s].x ^ mbits) | (raw[s].y ^ mbits) | (raw[s].z ^ mbits) | (raw[s].w ^ mbits);
+      if (__ballot(other != 0u) == 0ull) {
+        // m_w >= thr_f: the wave has hits, every one of them equal to m_w
+        flags |= kFlagUniform;
+        count = (uint32_t)max(0, min(4 * q_hi, n) - 4 * q_lo);
+      } else {
 #pragma unroll
       for (int s = 0; s < kS1; ++s) {
         const int nv = nvalid(s);
@@ -1264,8 +1291,9 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
         }
         count += slot_cnt;
       }
+      }
     }
-    if (count > cap) {
+    if (count > cap && !(flags & kFlagUniform)) {
       flags |= kFlagOverflow;
       count = cap;
     }
@@ -1351,7 +1379,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
     wi.kmax_idx = kmax_idx;
     wi.best_s = best_s;
     wi.best_idx = best_idx;
-    wi.pad = 0u;
+    wi.first = (flags & kFlagUniform) ? (uint32_t)(c0 + 4 * q_lo) : 0u;
     P.info[seg] = wi;
   }
 }
@@ -1749,6 +1777,13 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
   const uint32_t j = (uint32_t)lane();
   // per_batch(sb, cnt, first, gs): kGatherB slices sb, sb + kRW, ... of this wave, with
   // entry `lane` of each already loaded into first[u]
+  // Entry jj (< its count) of slice sl: loaded from the slice, or made up for a uniform one
+  // (which stores nothing and may count past the slice capacity).
+  auto entry = [&](int sl, const uint2* gsl, uint32_t jj) -> uint2 {
+    const uint32_t uk = sm.ukey[sl];
+    if (uk) return make_uint2(uk, sm.ufirst[sl] + jj);
+    return gsl[jj];
+  };
   auto batches = [&](auto per_batch) {
     for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
       uint32_t cnt[kGatherB];
@@ -1762,21 +1797,21 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
       for (int u = 0; u < kGatherB; ++u) {
         first[u] = make_uint2(0, 0);
-        if (j < cnt[u]) first[u] = gs[(int64_t)u * kRW * P.cap_w + j];
+        if (j < cnt[u]) first[u] = entry(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, j);
       }
       per_batch(sb, cnt, first, gs);
     }
   };
-  // f(jj, w, ok) over a slice's entries in id order, 64 per (wave-uniform) call; entries
-  // past the first 64 load 8 rounds at a time
-  auto slice_chunks = [&](const uint2* gsl, uint32_t cnt, uint2 first, auto f) {
+  // f(jj, w, ok) over the entries of slice sl in id order, 64 per (wave-uniform) call;
+  // entries past the first 64 load 8 rounds at a time
+  auto slice_chunks = [&](int sl, const uint2* gsl, uint32_t cnt, uint2 first, auto f) {
     f(j, first, j < cnt);
     for (uint32_t j0 = 64; j0 < cnt; j0 += 64 * 8) {
       uint2 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const uint32_t jj = j0 + 64 * u + j;
-        v[u] = jj < cnt ? gsl[jj] : make_uint2(0, 0);
+        v[u] = jj < cnt ? entry(sl, gsl, jj) : make_uint2(0, 0);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1794,7 +1829,7 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
       if (o >= nk) break;   // slices are in id order
       const uint32_t c = min(sm.segoff[sl + 1], nk) - o;
       const uint2* gsl = base + (int64_t)sl * P.cap_w;
-      slice_chunks(gsl, c, j < c ? gsl[j] : make_uint2(0, 0), [&](uint32_t jj, uint2 w, bool ok) {
+      slice_chunks(sl, gsl, c, j < c ? entry(sl, gsl, j) : make_uint2(0, 0), [&](uint32_t jj, uint2 w, bool ok) {
         if (ok) {
           sm.ckey[o + jj] = w.x;
           sm.cidx[o + jj] = w.y;
@@ -1804,11 +1839,18 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
     bar();
     return nk;
   }
-  // pass 1: first-digit histogram of every candidate
-  batches([&](int, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
+  // the key of slice sl when it is uniform, else 0 (wave-uniform)
+  auto ukey_of = [&](int sl) { return sl < nseg ? sm.ukey[sl] : 0u; };
+  // pass 1: first-digit histogram of every candidate (a uniform slice in one addition)
+  batches([&](int sb, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
-      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+      const uint32_t uk = ukey_of(sb + u * kRW);
+      if (uk) {
+        if (j == 0 && cnt[u]) atomicAdd(&sm.hist[(uk >> g.sh) & g.dm], cnt[u]);
+        continue;
+      }
+      slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
         if (ok) hist_add(sm.hist, (w.x >> g.sh) & g.dm);
       });
     }
@@ -1823,9 +1865,14 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
       uint32_t c = 0;
-      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
-        c += (uint32_t)__popcll(__ballot(ok && w.x >= thr_key));
-      });
+      const uint32_t uk = ukey_of(sb + u * kRW);
+      if (uk) {
+        c = uk >= thr_key ? cnt[u] : 0u;
+      } else {
+        slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+          c += (uint32_t)__popcll(__ballot(ok && w.x >= thr_key));
+        });
+      }
       const int sl = sb + u * kRW;
       if (j == 0 && sl < nseg) sm.kkey[sl] = c;
     }
@@ -1854,7 +1901,18 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
       uint32_t pos = sm.kkey[min(sb + u * kRW, nseg - 1)];
-      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+      const uint32_t uk = ukey_of(sb + u * kRW);
+      if (uk) {   // every entry is kept or none is
+        if (uk >= thr_key) {
+          const uint32_t uf = sm.ufirst[sb + u * kRW];
+          for (uint32_t jj = j; jj < cnt[u] && pos + jj < nf; jj += 64) {
+            sm.ckey[pos + jj] = uk;
+            sm.cidx[pos + jj] = uf + jj;
+          }
+        }
+        continue;
+      }
+      slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
         const bool keep = ok && w.x >= thr_key;
         const uint64_t bal = __ballot(keep);
         const uint32_t at = pos + mbcnt(bal);
@@ -2373,7 +2431,11 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       kmax = max(kmax, wi.kmax);
       thr_max = max(thr_max, wi.thr);
       cmin = min(cmin, wi.thr);
-      if (i < kMaxSeg) sm.segoff[i] = wi.count;
+      if (i < kMaxSeg) {
+        sm.segoff[i] = wi.count;
+        sm.ukey[i] = (wi.flags & kFlagUniform) ? wi.kmax : 0u;
+        sm.ufirst[i] = wi.first;
+      }
     }
     rp = plan_row(P, MODE, r);
   }
@@ -2549,7 +2611,8 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     const bool fast = !P.force_exact && (flags & kFlagOverflow) == 0 && total >= ke;
     uint32_t ntot = 0, lo_key = cmin;
     bool pre = false;
-    if (fast && total <= (uint32_t)kLdsCand) {
+    // rows holding a uniform slice take the filtered gather, the one that reads them
+    if (fast && total <= (uint32_t)kLdsCand && !(flags & kFlagUniform)) {
       bar();
       // The top-k select's first pass is counted while the candidates are written to LDS:
       // every candidate key lies in [cmin, kmax], so its digit needs no prefix test.
@@ -2837,7 +2900,11 @@ bool make_plan(int64_t rows, int64_t V, Plan& pl, int64_t cap_limit = kCapW) {
   pl.chunk_len = len;
   pl.chunks = (V + len - 1) / len;
   const int64_t qw = ((len + 3) / 4 + kW1 - 1) / kW1;   // quads per wave
-  pl.cap_w = 4 * qw < cap_limit ? 4 * qw : cap_limit;
+  const int64_t share = 4 * qw;                          // elements per wave, at most
+  // half the share, less 32 entries: the summaries, partial sums and per-row histograms
+  // then fit too, so that a default-chunked workspace is no larger than the logits
+  const int64_t cap = share <= kCapSmall ? share : std::max<int64_t>(share / 2 - 32, kCapSmall);
+  pl.cap_w = std::min<int64_t>(cap, cap_limit);
   const int64_t rr = rows > 0 ? rows : 1;
   if (rr * pl.chunks * kW1 > (int64_t)0x7FFFFFFF) return false;
   const size_t nseg = (size_t)(rr * pl.chunks * kW1);
