@@ -193,8 +193,6 @@ struct Smem {
   uint32_t kkey[kFastK];       // the kept set P, compacted for the Gumbel draws
   uint32_t kidx[kFastK];
   uint32_t segoff[kMaxSeg + 1];
-  uint32_t ukey[kMaxSeg];      // per slice: its key when it is uniform, else 0 (no real key is 0)
-  uint32_t ufirst[kMaxSeg];    // per uniform slice: the id of its first entry
   uint32_t red[4 * kRW];
   uint64_t red64[2 * kRW];
   float reds[kRW];
@@ -1777,13 +1775,6 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
   const uint32_t j = (uint32_t)lane();
   // per_batch(sb, cnt, first, gs): kGatherB slices sb, sb + kRW, ... of this wave, with
   // entry `lane` of each already loaded into first[u]
-  // Entry jj (< its count) of slice sl: loaded from the slice, or made up for a uniform one
-  // (which stores nothing and may count past the slice capacity).
-  auto entry = [&](int sl, const uint2* gsl, uint32_t jj) -> uint2 {
-    const uint32_t uk = sm.ukey[sl];
-    if (uk) return make_uint2(uk, sm.ufirst[sl] + jj);
-    return gsl[jj];
-  };
   auto batches = [&](auto per_batch) {
     for (int sb = wave(); sb < nseg; sb += kRW * kGatherB) {
       uint32_t cnt[kGatherB];
@@ -1797,21 +1788,21 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
       for (int u = 0; u < kGatherB; ++u) {
         first[u] = make_uint2(0, 0);
-        if (j < cnt[u]) first[u] = entry(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, j);
+        if (j < cnt[u]) first[u] = gs[(int64_t)u * kRW * P.cap_w + j];
       }
       per_batch(sb, cnt, first, gs);
     }
   };
-  // f(jj, w, ok) over the entries of slice sl in id order, 64 per (wave-uniform) call;
-  // entries past the first 64 load 8 rounds at a time
-  auto slice_chunks = [&](int sl, const uint2* gsl, uint32_t cnt, uint2 first, auto f) {
+  // f(jj, w, ok) over a slice's entries in id order, 64 per (wave-uniform) call; entries
+  // past the first 64 load 8 rounds at a time
+  auto slice_chunks = [&](const uint2* gsl, uint32_t cnt, uint2 first, auto f) {
     f(j, first, j < cnt);
     for (uint32_t j0 = 64; j0 < cnt; j0 += 64 * 8) {
       uint2 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const uint32_t jj = j0 + 64 * u + j;
-        v[u] = jj < cnt ? entry(sl, gsl, jj) : make_uint2(0, 0);
+        v[u] = jj < cnt ? gsl[jj] : make_uint2(0, 0);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1829,7 +1820,7 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
       if (o >= nk) break;   // slices are in id order
       const uint32_t c = min(sm.segoff[sl + 1], nk) - o;
       const uint2* gsl = base + (int64_t)sl * P.cap_w;
-      slice_chunks(sl, gsl, c, j < c ? entry(sl, gsl, j) : make_uint2(0, 0), [&](uint32_t jj, uint2 w, bool ok) {
+      slice_chunks(gsl, c, j < c ? gsl[j] : make_uint2(0, 0), [&](uint32_t jj, uint2 w, bool ok) {
         if (ok) {
           sm.ckey[o + jj] = w.x;
           sm.cidx[o + jj] = w.y;
@@ -1839,18 +1830,11 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
     bar();
     return nk;
   }
-  // the key of slice sl when it is uniform, else 0 (wave-uniform)
-  auto ukey_of = [&](int sl) { return sl < nseg ? sm.ukey[sl] : 0u; };
-  // pass 1: first-digit histogram of every candidate (a uniform slice in one addition)
-  batches([&](int sb, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
+  // pass 1: first-digit histogram of every candidate
+  batches([&](int, const uint32_t (&cnt)[kGatherB], const uint2 (&first)[kGatherB], const uint2* gs) {
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
-      const uint32_t uk = ukey_of(sb + u * kRW);
-      if (uk) {
-        if (j == 0 && cnt[u]) atomicAdd(&sm.hist[(uk >> g.sh) & g.dm], cnt[u]);
-        continue;
-      }
-      slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
         if (ok) hist_add(sm.hist, (w.x >> g.sh) & g.dm);
       });
     }
@@ -1865,14 +1849,9 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
       uint32_t c = 0;
-      const uint32_t uk = ukey_of(sb + u * kRW);
-      if (uk) {
-        c = uk >= thr_key ? cnt[u] : 0u;
-      } else {
-        slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
-          c += (uint32_t)__popcll(__ballot(ok && w.x >= thr_key));
-        });
-      }
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+        c += (uint32_t)__popcll(__ballot(ok && w.x >= thr_key));
+      });
       const int sl = sb + u * kRW;
       if (j == 0 && sl < nseg) sm.kkey[sl] = c;
     }
@@ -1901,18 +1880,7 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
 #pragma unroll
     for (int u = 0; u < kGatherB; ++u) {
       uint32_t pos = sm.kkey[min(sb + u * kRW, nseg - 1)];
-      const uint32_t uk = ukey_of(sb + u * kRW);
-      if (uk) {   // every entry is kept or none is
-        if (uk >= thr_key) {
-          const uint32_t uf = sm.ufirst[sb + u * kRW];
-          for (uint32_t jj = j; jj < cnt[u] && pos + jj < nf; jj += 64) {
-            sm.ckey[pos + jj] = uk;
-            sm.cidx[pos + jj] = uf + jj;
-          }
-        }
-        continue;
-      }
-      slice_chunks(sb + u * kRW, gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
+      slice_chunks(gs + (int64_t)u * kRW * P.cap_w, cnt[u], first[u], [&](uint32_t, uint2 w, bool ok) {
         const bool keep = ok && w.x >= thr_key;
         const uint64_t bal = __ballot(keep);
         const uint32_t at = pos + mbcnt(bal);
@@ -1926,6 +1894,31 @@ __device__ __forceinline__ uint32_t gather_filtered(const Params& P, int r, int 
   });
   bar();
   return nf;
+}
+
+// The top ke candidates of a row whose candidates all hold one key (kmax == every slice's
+// threshold) when some of its slices are uniform (they store nothing): the first ke
+// candidates in id order, read from the stored slices or made up from the uniform ones (whose
+// key and first id are in their wave summaries). Returns the number gathered.
+__device__ __forceinline__ uint32_t gather_equal(const Params& P, int r, int nseg, uint32_t ke, Smem& sm) {
+  const uint2* base = P.cand + (int64_t)r * nseg * P.cap_w;
+  const WaveInfo* inf = P.info + (int64_t)r * nseg;
+  const uint32_t nk = min(sm.segoff[nseg], ke);
+  for (int sl = wave(); sl < nseg; sl += kRW) {
+    const uint32_t o = sm.segoff[sl];
+    if (o >= nk) break;   // slices are in id order
+    const uint32_t c = min(sm.segoff[sl + 1], nk) - o;
+    const WaveInfo wi = inf[sl];
+    const bool uni = (wi.flags & kFlagUniform) != 0;
+    const uint2* gsl = base + (int64_t)sl * P.cap_w;
+    for (uint32_t jj = (uint32_t)lane(); jj < c; jj += 64) {
+      const uint2 w = uni ? make_uint2(wi.kmax, wi.first + jj) : gsl[jj];
+      sm.ckey[o + jj] = w.x;
+      sm.cidx[o + jj] = w.y;
+    }
+  }
+  bar();
+  return nk;
 }
 
 // ------------------------------------------------------------------ nucleus pass
@@ -2431,11 +2424,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       kmax = max(kmax, wi.kmax);
       thr_max = max(thr_max, wi.thr);
       cmin = min(cmin, wi.thr);
-      if (i < kMaxSeg) {
-        sm.segoff[i] = wi.count;
-        sm.ukey[i] = (wi.flags & kFlagUniform) ? wi.kmax : 0u;
-        sm.ufirst[i] = wi.first;
-      }
+      if (i < kMaxSeg) sm.segoff[i] = wi.count;
     }
     rp = plan_row(P, MODE, r);
   }
@@ -2611,8 +2600,16 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     const bool fast = !P.force_exact && (flags & kFlagOverflow) == 0 && total >= ke;
     uint32_t ntot = 0, lo_key = cmin;
     bool pre = false;
-    // rows holding a uniform slice take the filtered gather, the one that reads them
-    if (fast && total <= (uint32_t)kLdsCand && !(flags & kFlagUniform)) {
+    if (fast && (flags & kFlagUniform)) {
+      // Some slice is uniform (it stores nothing). When every candidate is one key its first
+      // ke in id order are the top ke; otherwise (a constant stretch among other candidates)
+      // the row takes the exact path.
+      if (cmin == kmax) {
+        bar();
+        ntot = gather_equal(P, r, nseg, ke, sm);
+        lo_key = kmax;
+      }
+    } else if (fast && total <= (uint32_t)kLdsCand) {
       bar();
       // The top-k select's first pass is counted while the candidates are written to LDS:
       // every candidate key lies in [cmin, kmax], so its digit needs no prefix test.
