@@ -49,8 +49,10 @@
  *     enqueued; ts_last_error() then holds a thread-local message.
  *   - Workspace: device memory of at least ts_workspace_bytes(op, rows, vocab, k_max)
  *     bytes, 256-byte aligned, owned by the caller. It needs no initialisation: every call
- *     writes what it later reads (per-wave chunk summaries, then candidate slices). One
- *     workspace serves one call at a time: calls that overlap on one workspace race.
+ *     writes what it later reads (per-wave chunk summaries, then candidate slices). With
+ *     the default chunking it is no larger than the logits it covers (the 64 x 151936
+ *     decode batch: 38.4 MB). One workspace serves one call at a time: calls that overlap
+ *     on one workspace race.
  *   - Results are deterministic: the same inputs give the same output bytes on every
  *     call, independent of how rows are split over workgroups.
  */
@@ -173,8 +175,8 @@ int ts_sample_rows(const float* logits, int64_t rows, int64_t vocab, int64_t row
  * same results (byte for byte) as ts_sample_rows, without the workspace: the library keeps it
  * in a static device array of 16 MiB per GPU (held from the library's load until the process
  * ends), found once per device with hipGetSymbolAddress. The call allocates nothing. Its
- * candidate slices hold 256 candidates per wave; rows whose waves publish more (massive ties)
- * take the exact path, which gives the same bytes at a higher cost.
+ * candidate slices hold at most 256 candidates per wave; rows whose waves publish more
+ * (massive ties) take the exact path, which gives the same bytes at a higher cost.
  * Limit: the batch must fit the scratch (about 8.4 KB per 8192-logit chunk of a row plus
  * 8.3 KB per row: the 64 x 151936 decode batch takes 11 MB); larger batches fail with
  * TS_ERR_INVALID_ARG and a message in ts_last_error, before any device work.
