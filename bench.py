@@ -445,6 +445,17 @@ def main():
     torch.cuda.synchronize()
     copy_ms = float(np.median([a.elapsed_time(b) for a, b in cps]))
 
+    # Known-size plain kernels for the FETCH_SIZE / WRITE_SIZE counters (profiles/): the
+    # read-ceiling kernel below reads B*V*4 bytes and writes a few KB; the workspace fill
+    # writes B*V*4 bytes. Both spread over every XCD, as the sampling kernels do. (The copy
+    # above is one blit kernel whose counted share differs from run to run.)
+    fill = torch.empty(BYTES_PER_CALL // 4, dtype=torch.int32, device=dev)
+    for i in range(5):
+        rc = lib.ts_workspace_init(fill.data_ptr(), BYTES_PER_CALL, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(ts.ts_last_error())
+    del fill
+
     # A plain read of the same buffers with the stream kernel's launch shape (the library's
     # diagnostic read kernel): the streaming ceiling the sampling call is compared against.
     # K back-to-back reads between one event pair, like region_us_per_call.

@@ -10,7 +10,7 @@ from gpu_helpers import banner, torch_cuda
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n", [1, 3, 8192, 1_000_003])
+@pytest.mark.parametrize("n", [1, 3, 8192, 1_000_003, 64 * 151936])
 def test_read_ceiling_reads_every_element(n):
     torch = torch_cuda()
     banner(f"read ceiling n={n}")
