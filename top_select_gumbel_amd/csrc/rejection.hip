@@ -365,26 +365,40 @@ __global__ void __launch_bounds__(kJT) ts_rejection_kernel(JParams P) {
   const float t = P.t ? P.t[r] : 1.0f;
   const float minp = P.minp ? P.minp[r] : 0.0f;
 
-  // Pass 1: maximum key, lowest id holding it, NaN.
+  // Pass 1: maximum key, NaN and, for greedy rows (T = 0), the lowest id holding the maximum.
   uint32_t bk = 0u, bid = 0xFFFFFFFFu, nan = 0u;
   {
     const int l = lane();
-    row_pass(R, P.nsub, [&](int sb, const float4* v) {
+    if (t == 0.0f) {
+      row_pass(R, P.nsub, [&](int sb, const float4* v) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t id0 = (uint32_t)(sb * 1024 + 256 * u + 4 * l);
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t id0 = (uint32_t)(sb * 1024 + 256 * u + 4 * l);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = qv(v[u], e);
-          const uint32_t key = f2key(x);
-          nan |= (x != x) ? 1u : 0u;
-          if (id0 + e < (uint32_t)P.V && key > bk) {
-            bk = key;
-            bid = id0 + e;
+          for (int e = 0; e < 4; ++e) {
+            const float x = qv(v[u], e);
+            const uint32_t key = f2key(x);
+            nan |= (x != x) ? 1u : 0u;
+            if (id0 + e < (uint32_t)P.V && key > bk) {
+              bk = key;
+              bid = id0 + e;
+            }
           }
         }
-      }
-    });
+      });
+    } else {
+      // The IEEE 754-2019 maximum propagates NaN: the running maximum is NaN exactly when the
+      // lane read one (tokens past the row end read as -inf).
+      float fm = -INFINITY;
+      row_pass(R, P.nsub, [&](int, const float4* v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          fm = __builtin_elementwise_maximum(fm, __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[u].x, v[u].y),
+                                                                              __builtin_elementwise_maximum(v[u].z, v[u].w)));
+      });
+      nan = __builtin_isnan(fm) ? 1u : 0u;
+      bk = nan ? 0u : f2key(fm);
+    }
     const uint32_t wk = wave_max(bk);
     const uint32_t wi = ~wave_max(bk == wk ? ~bid : 0u);
     const uint32_t wn = wave_max(nan);
