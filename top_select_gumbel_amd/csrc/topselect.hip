@@ -129,6 +129,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // kept tokens above the cut bin, as (ordered score << 32 | ~id) so that the maximum prefers
 // the lowest id on equal scores, and the number of cut-bin tokens listed (the list itself
 // lives in the row's candidate slices, which nucleus rows leave unused).
+constexpr int kSplitCUs = 256;   // row-kernel workgroups that fill the chip (one per CU: its LDS)
 constexpr int kNucBins = 1024;   // nucleus bins (value-linear window below the maximum, and bin 0)
 struct NucRow {
   uint64_t mass[kNucBins];     // exact fixed-point mass per bin
@@ -136,7 +137,8 @@ struct NucRow {
   uint32_t nlist;              // tokens of the cut bin, listed by the cut pass
   uint32_t nabove;             // tokens in bins above the cut bin
   uint32_t kabove;             // of those, the ones min-p keeps (all of them without min-p)
-  uint32_t pad[3];
+  uint32_t ticket;             // split nucleus: workgroups of the row that finished their part
+  uint32_t pad[2];
 };
 static_assert(sizeof(NucRow) % 16 == 0, "NucRow is zeroed in 16-byte words");
 
@@ -161,6 +163,7 @@ struct Params {
   int32_t force_exact;
   int32_t direct;              // rows of <= kLdsCand logits: the row kernel alone, row in LDS
   int32_t nucleus;             // top-k off for every row: the nucleus pass spreads top-p work
+  int32_t split;               // workgroups per row of the row kernel's split nucleus (0: none)
   struct NucRow* nuc;          // per row: the nucleus pass's histograms
   int32_t* out_idx;
   int32_t* out_kept;
@@ -242,6 +245,12 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int mode, int r) {
   else if (P.nucleus && rp.k_eff == P.V) rp.path = kPathNucleus;
   else rp.path = kPathStream;
   return rp;
+}
+
+// Rows of the row kernel's split nucleus: calls with a top-k array whose value for the row
+// reaches the row length (top-k off, visible on the device only), with top-p or min-p on.
+__device__ __forceinline__ bool split_row(const Params& P, const RowPlan& rp) {
+  return P.split && rp.path == kPathStream && rp.k_eff >= rp.n && (rp.p != 1.0f || rp.minp > 0.0f);
 }
 
 // ------------------------------------------------------------------ selection descriptor
@@ -1361,6 +1370,7 @@ __global__ __launch_bounds__(kT1) __attribute__((amdgpu_waves_per_eu(7))) void t
   if (MODE == kModeTopp && P.out_mask) {
     fill_bytes_nt<kT1>(P.out_mask + (int64_t)r * P.V + c0, n, (path == kPathFull) ? (uint8_t)1 : (uint8_t)0);
   }
+  if (c == 0 && tid == 0 && split_row(P, rp)) P.nuc[r].ticket = 0u;   // the split nucleus's counter
   if (path == kPathNucleus) {
     // this workgroup's share of zeroing the row's nucleus histograms
     uint4* z = reinterpret_cast<uint4*>(P.nuc + r);
@@ -2241,6 +2251,331 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   }
 }
 
+// f(v, q, live) for the quads q in [qa, qb) of a row of V elements (elements past V read as
+// -inf), in rounds of 8 quads per thread: quads base + u * kRT + tid, u < 8, with the round
+// index uniform over the workgroup so that f may use wave-wide operations (every lane calls it
+// each round; `live` tells whether its quad exists). An aligned row takes 16-byte loads of its
+// whole quads, the next round's issued before this round is visited (indexes clamped into the
+// row, so every load is in bounds; quads past the range are replaced by -inf with selects, so
+// that no other load stands between a round's loads and their use), then a partial last quad
+// in a round of its own by element loads; an unaligned row takes element loads.
+template <class F>
+__device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32_t qa, uint32_t qb, F f) {
+  constexpr uint32_t kStep = kRT * 8;
+  const uint32_t nfull = V >> 2;
+  auto slow = [&](uint32_t a, uint32_t b) {
+    for (uint32_t base = a; base < b; base += kStep) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = base + u * kRT + threadIdx.x;
+        v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (q < b) {
+          v[u].x = row[4 * q];
+          if (4 * q + 1 < V) v[u].y = row[4 * q + 1];
+          if (4 * q + 2 < V) v[u].z = row[4 * q + 2];
+          if (4 * q + 3 < V) v[u].w = row[4 * q + 3];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = base + u * kRT + threadIdx.x;
+        f(v[u], q, q < b);
+      }
+    }
+  };
+  if (((uintptr_t)row & 15u) != 0 || nfull == 0) {
+    slow(qa, qb);
+    return;
+  }
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  const uint32_t qe = min(qb, nfull);       // the range's whole quads end here
+  auto load = [&](float4 (&v)[8], uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = row4[min(base + u * kRT + threadIdx.x, nfull - 1u)];
+  };
+  float4 v[8];
+  if (qa < qe) load(v, qa);
+  for (uint32_t base = qa; base < qe; base += kStep) {
+    float4 nx[8];
+    load(nx, base + kStep);          // unconditional (clamped), so the waits below count it
+    asm volatile("" ::: "memory");   // keep the next round's loads issued ahead of this round's work
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t q = base + u * kRT + threadIdx.x;
+      const bool in = q < qe;
+      const float4 w = make_float4(in ? v[u].x : -INFINITY, in ? v[u].y : -INFINITY, in ? v[u].z : -INFINITY,
+                                   in ? v[u].w : -INFINITY);
+      f(w, q, in);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = nx[u];
+  }
+  if (qb > qe && qb > qa) slow(max(qa, qe), qb);   // the partial last quad
+}
+
+// Top-p (and min-p after it) over whole rows whose k reaches the row length, in calls with a
+// top-k array (the host cannot see the array's values, so the nucleus passes over the chunk
+// workgroups do not run for them). The row kernel runs P.split workgroups per row; each takes
+// a contiguous part of the row and, with the row maximum m known from the wave summaries:
+//  - bins every token's exact fixed-point mass by value in the window below m (nuc_bin; bin 0
+//    below the window, summed in registers) and adds the part's bins to the row's histogram;
+//  - sampling: draws the Gumbel score of every token of the window that min-p keeps (one
+//    Philox block per quad) and keeps the best per bin (p == 1: one best for the row), since
+//    the kept set is every bin above the cut plus a prefix of the cut bin, whichever bin that
+//    turns out to be.
+// Each part stores its bins (plain stores) into its own slot in the row's candidate area, which
+// rows of this kind leave unused. The last workgroup of the row to finish its part (a counter;
+// no workgroup ever waits for another) then sums the slots, finds the cut bin where the mass from the top reaches ceil(p * Z), lists that
+// bin's tokens in LDS from one compare-only read of the row (top-p masks: also marks the
+// tokens above the cut), and takes the exact cut inside it with the same fixed-point select
+// as the exact path. The sampled token is the best of the bins above the cut and of the
+// selected members of the cut bin. Returns false only in the finishing workgroup, when the cut
+// bin holds more tokens than the LDS list (the caller then takes the row-streaming path, which
+// writes the same mask bytes).
+template <int MODE>
+__device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
+                                            uint64_t seed, Smem& sm, double lse, int part) {
+  const float* row = P.x + (int64_t)r * P.stride;
+  const uint32_t V = (uint32_t)rp.n;
+  const float m = key2f(kmax);
+  const float t = rp.t;
+  const double c2 = kLog2e / (double)t;
+  const int S = 63 - bitlen(V);
+  const bool minp_on = rp.minp > 0.0f;
+  const bool binned = rp.p != 1.0f;          // p == 1: min-p alone keeps every token it passes
+  auto wmass = [&](uint32_t rk) { return mass32_of(weight32(rk, m, c2), S); };
+  auto ok = [&](uint32_t rk) { return !minp_on || weight32(rk, m, c2) >= rp.minp; };
+  const NucBin nb = nuc_bin_params(m, rp.p, t, (int)V);
+  NucRow* nr = P.nuc + r;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int G = P.split;
+  // the parts' slots: 2 * kNucBins words each, masses then best scores
+  uint64_t* slots = reinterpret_cast<uint64_t*>(P.cand + (int64_t)r * P.chunks * kW1 * P.cap_w);
+  const uint32_t nq = (V + 3) >> 2;
+  const uint32_t per = (nq + (uint32_t)G - 1) / (uint32_t)G;
+  const uint32_t qa = min(nq, (uint32_t)part * per), qb = min(nq, qa + per);
+  uint64_t* bbest = sm.mhi + kNucBins;      // the upper half of the mass histogram (zero)
+
+  // ---- this workgroup's part: masses by bin, and the best score per bin
+  uint64_t z0 = 0, best = 0;
+  visit_quads(row, V, qa, qb, [&](const float4& v, uint32_t q, bool live) {
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    uint32_t bin[4];
+    bool cand[4];
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bin[e] = binned ? nuc_bin(xs[e], nb) : 1u;
+      if (binned && live) {
+        const uint64_t q64 = mass32_of(weightf(xs[e], m, c2), S);   // 0 for the -inf past the row end
+        if (bin[e] == 0u) z0 += q64;
+        else if (q64) atomicAdd((unsigned long long*)&sm.mhi[bin[e]], (unsigned long long)q64);
+      }
+      cand[e] = MODE == kModeSample && live && 4 * q + e < V && bin[e] != 0u && ok(f2key(xs[e]));
+      any |= cand[e];
+    }
+    if (MODE == kModeSample && any) {
+      const uint4 w = philox4x32_10(q, (uint32_t)r, k0, k1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cand[e]) {
+          const float g = gumbel_from_uniform(uniform_from_word(pick_word(w, (uint32_t)e)));
+          const float sc = (xs[e] - m) / t + g;
+          const uint64_t pk = ((uint64_t)f2key(sc) << 32) | (uint32_t)~(4 * q + e);
+          if (binned) atomicMax((unsigned long long*)&bbest[bin[e]], (unsigned long long)pk);
+          else best = max(best, pk);
+        }
+      }
+    }
+  });
+  {
+    uint64_t zl = 0;
+    block_sum2_u64<kRW>(z0, zl, sm.red64);   // its barriers also complete the LDS atomics
+  }
+  uint64_t* mine = slots + (int64_t)part * 2 * kNucBins;
+  static_assert(kNucBins == 2 * kRT, "two bins per thread");
+  // The slots are written with device-scope atomic stores, which write through to the point
+  // of coherence of all XCDs, and read with device-scope atomic loads: once every store has
+  // completed (the wait below), the part is published without a cache write-back fence.
+  auto put = [&](uint64_t* a, uint64_t v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  if (binned) {
+    const int i = 2 * (int)threadIdx.x;
+    put(mine + i, sm.mhi[i] + (threadIdx.x == 0 ? z0 : 0ull));
+    put(mine + i + 1, sm.mhi[i + 1]);
+    sm.mhi[i] = 0;
+    sm.mhi[i + 1] = 0;
+    if (MODE == kModeSample) {
+      put(mine + kNucBins + i, bbest[i]);
+      put(mine + kNucBins + i + 1, bbest[i + 1]);
+      bbest[i] = 0;
+      bbest[i + 1] = 0;
+    }
+  } else if (MODE == kModeSample) {
+    uint32_t hi = (uint32_t)(best >> 32);
+    hi = block_max_u32<kRW>(hi, sm.red);
+    uint32_t lo = ((uint32_t)(best >> 32) == hi) ? (uint32_t)best : 0u;
+    lo = block_max_u32<kRW>(lo, sm.red);
+    if (threadIdx.x == 0) put(mine + kNucBins, ((unsigned long long)hi << 32) | lo);
+  }
+  // publish the part (every store complete), then count it; the workgroup that counts last
+  // finishes the row
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  bar();
+  if (threadIdx.x == 0) sm.res[3] = __hip_atomic_fetch_add(&nr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bar();
+  const bool last = sm.res[3] == (uint32_t)(G - 1);
+  bar();
+  if (!last) return true;
+
+  // ---- the row's finish: the cut bin from the whole histogram
+  int cut = -1;                 // bins above it are kept whole; p == 1: every token
+  uint64_t target = 0, ma = 0;
+  if (binned) {
+    const int i = 2 * (int)threadIdx.x;
+    uint64_t m0 = 0, m1 = 0, zl = 0;
+    for (int g = 0; g < G; ++g) {
+      m0 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      m1 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sm.mhi[i] = m0;
+    sm.mhi[i + 1] = m1;
+    uint64_t zh = m0 + m1;
+    block_sum2_u64<kRW>(zh, zl, sm.red64);
+    target = topp_target(rp.p, zh);
+    search_mass(sm, target, 0ull);           // also clears the histograms for the exact cut
+    cut = (int)sm.res[0];
+    ma = sm.res64[0];
+  }
+  // the cut bin as a key range [ka, kb): nuc_bin is monotone in the value up to m
+  auto first_key = [&](uint32_t b) {        // smallest key <= kmax whose bin is >= b, else kmax + 1
+    uint32_t lo = kKeyNegInf, hi = kmax + 1u;
+    while (lo < hi) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      if (nuc_bin(key2f(mid), nb) >= b) hi = mid;
+      else lo = mid + 1u;
+    }
+    return lo;
+  };
+  const uint32_t ka = binned ? first_key((uint32_t)cut) : kKeyNegInf;
+  const uint32_t kb = binned ? first_key((uint32_t)cut + 1u) : kKeyNegInf;
+  // one read of the row: the cut bin's tokens into the LDS list; top-p masks also mark the
+  // tokens above the cut that min-p keeps
+  uint8_t* mrow = (MODE == kModeTopp && P.out_mask) ? P.out_mask + (int64_t)r * P.V : nullptr;
+  uint32_t n_up = 0, k_up = 0;
+  // as values: x >= xb is key >= kb, and x >= xa is key >= ka (keys order the values, -0 as +0)
+  const float xa = key2f(ka), xb = key2f(kb);
+  if (binned || MODE == kModeTopp) visit_quads(row, V, 0u, nq, [&](const float4& v, uint32_t q, bool live) {
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    const float qmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v.x, v.y), __builtin_elementwise_maximum(v.z, v.w));
+    const float qmin = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v.x, v.y), __builtin_elementwise_minimum(v.z, v.w));
+    bool inl[4] = {false, false, false, false};
+    uint32_t nin = 0;
+    if (binned) {
+      // xb > -inf here, so the -inf that pads a quad is never above the cut
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n_up += xs[e] >= xb ? 1u : 0u;
+      if (qmax >= xa && qmin < xb) {   // some token of the quad may lie in the cut bin
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          inl[e] = live && 4 * q + e < V && xs[e] >= xa && xs[e] < xb;
+          nin += inl[e] ? 1u : 0u;
+        }
+      }
+    }
+    if (MODE == kModeTopp && qmax >= xb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = live && 4 * q + e < V && xs[e] >= xb && ok(f2key(xs[e]));
+        k_up += keep ? 1u : 0u;
+        if (keep && mrow) mrow[4 * q + e] = 1;
+      }
+    }
+    const uint64_t any = __ballot(nin != 0u);
+    if (any) {   // cut-bin tokens: one LDS reservation per wave and round
+      const uint32_t incl = wave_incl_scan(nin);
+      const uint32_t tot = wave_total(incl);
+      uint32_t wb = 0;
+      if (lane() == 0) wb = atomicAdd(&sm.bcount, tot);
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb) + incl - nin;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (inl[e]) {
+          if (pos < (uint32_t)kLdsCand) {
+            sm.ckey[pos] = f2key(xs[e]);
+            sm.cidx[pos] = 4 * q + e;
+          }
+          ++pos;
+        }
+      }
+    }
+  });
+  bar();
+  const uint32_t nlist = sm.bcount;
+  bar();
+  if (threadIdx.x == 0) sm.bcount = 0;   // zero again outside the small-bin collections
+  bar();
+  if (nlist > (uint32_t)kLdsCand) return false;
+  uint64_t un = n_up, uk = k_up;
+  block_sum2_u64<kRW>(un, uk, sm.red64);
+  Sel sp = sel_all();
+  if (binned) {
+    // the exact cut inside the cut bin (a bin is a contiguous key range)
+    uint32_t top_key = 0u, base_key = 0xFFFFFFFFu;
+    for (uint32_t i = threadIdx.x; i < nlist; i += kRT) {
+      top_key = max(top_key, sm.ckey[i]);
+      base_key = min(base_key, sm.ckey[i]);
+    }
+    top_key = block_max_u32<kRW>(top_key, sm.red);
+    base_key = block_min_u32<kRW>(base_key, sm.red);
+    uint32_t kept_unused;
+    sp = select_mass<false>(LdsVis{sm.ckey, sm.cidx, nlist}, wmass, target, nlist, top_key, base_key, 0u, V - 1,
+                            sm, kept_unused, false, ma, (uint32_t)un);
+  }
+  if (MODE == kModeTopp) {
+    uint64_t c = threadIdx.x == 0 ? uk : 0ull, z = 0;
+    for (uint32_t i = threadIdx.x; i < nlist; i += kRT) {
+      if (sel_member(sp, sm.ckey[i], sm.cidx[i]) && ok(sm.ckey[i])) {
+        c += 1;
+        if (mrow) mrow[sm.cidx[i]] = 1;
+      }
+    }
+    block_sum2_u64<kRW>(c, z, sm.red64);
+    if (threadIdx.x == 0) P.out_kept[r] = (int32_t)c;
+  } else if (MODE == kModeSample) {
+    uint64_t bst = 0;
+    if (binned) {
+      for (int i = cut + 1 + (int)threadIdx.x; i < kNucBins; i += kRT)
+        for (int g = 0; g < G; ++g)
+          bst = max(bst, (uint64_t)__hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + kNucBins + i, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+      for (uint32_t i = threadIdx.x; i < nlist; i += kRT) {
+        const uint32_t key = sm.ckey[i], id = sm.cidx[i];
+        if (sel_member(sp, key, id) && ok(key)) {
+          const float sc = gumbel_score(key, id, m, t, (uint32_t)r, k0, k1);
+          bst = max(bst, ((uint64_t)f2key(sc) << 32) | (uint32_t)~id);
+        }
+      }
+    } else {
+      for (int g = threadIdx.x; g < G; g += kRT)
+        bst = max(bst, (uint64_t)__hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + kNucBins, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    }
+    uint32_t hi = (uint32_t)(bst >> 32);
+    hi = block_max_u32<kRW>(hi, sm.red);
+    uint32_t lo = ((uint32_t)(bst >> 32) == hi) ? (uint32_t)bst : 0u;
+    lo = block_max_u32<kRW>(lo, sm.red);
+    const int32_t tok = (int32_t)~lo;
+    if (threadIdx.x == 0) {
+      P.out_token[r] = tok;
+      put_logp(P, r, tok, t, lse);
+    }
+  }
+  return true;
+}
+
 // The row kernel's side of a NUCLEUS row (both nucleus passes done): Z and the cut bin come
 // from the row's histograms exactly as the second pass found them; the cut bin's tokens come
 // from the row's list into LDS for the exact cut, the same fixed-point select as the exact
@@ -2389,7 +2724,12 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   // being dealt round-robin over the 8 XCDs), workgroup b takes a row whose summaries and
   // candidates were written on its own XCD.
   const int b = (int)blockIdx.x;
-  const int r = P.xcd_map ? (b & 7) * (P.rows >> 3) + (b >> 3) : b;
+  // workgroups past the rows are the other parts of split-nucleus rows (part 1 of every row,
+  // then part 2, ...); for the other rows they end here
+  const int part = b < P.rows ? 0 : 1 + (b - P.rows) / P.rows;
+  const int bb = part ? (b - P.rows) % P.rows : b;
+  const int r = P.xcd_map ? (bb & 7) * (P.rows >> 3) + (bb >> 3) : bb;
+  if (part && !split_row(P, plan_row(P, MODE, r))) return;
   const int nseg = P.chunks * kW1;
   const WaveInfo* inf = P.info + (int64_t)r * nseg;
   uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
@@ -2445,7 +2785,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     st = TS_ROW_NONFINITE;
   }
   if (st == TS_ROW_OK) st = rp.bad;
-  if (threadIdx.x == 0 && P.status) P.status[r] = st;
+  if (part == 0 && threadIdx.x == 0 && P.status) P.status[r] = st;
   // Sampling with logprobs: lse = m/T + log S over the whole row, S combined from the wave
   // shares in wave order, each rescaled from its wave maximum to the row maximum m.
   double lse = 0.0;
@@ -2480,6 +2820,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     bar_all();
   }
   if (st != TS_ROW_OK) {
+    if (part) return;
     if (MODE == kModeTopp && rp.path == kPathFull && P.out_mask && !P.direct) {
       fill_bytes_nt<kRT>(P.out_mask + (int64_t)r * P.V, P.V, 0);   // chunks had written ones
     }
@@ -2787,6 +3128,9 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       }
     }
   }
+  // top-k off (k >= the row length) with top-p or min-p on, in a call with a top-k array: the
+  // split nucleus over this row's workgroups (the exact path when its cut bin is too long)
+  if (split_row(P, rp) && row_nucleus<MODE>(P, rp, r, kmax, seed, sm, lse, part)) return;
   row_stream<MODE>(P, rp, r, kmax, kfloor, seed, sm, lse);
 }
 
@@ -2965,6 +3309,15 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   // No top-k array: every row has top-k off, so rows with top-p or min-p on take the
   // nucleus pass (spread over the chunk workgroups) instead of one workgroup streaming the row.
   P.nucleus = (MODE != kModeTopk && !P.direct && !P.force_exact && k == nullptr && (p != nullptr || minp != nullptr)) ? 1 : 0;
+  // With a top-k array, rows whose k reaches the row length are seen on the device only: the
+  // row kernel then runs up to 8 workgroups per row (one per CU across the batch) that share
+  // such rows' nucleus work; for the other rows the extra workgroups end at once.
+  // Each part keeps its bins in a slot of 2 * kNucBins words inside the row's candidate area.
+  const int64_t slots = pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2) / (2 * kNucBins * (int64_t)sizeof(uint64_t));
+  const int64_t split = std::min<int64_t>({8, std::max<int64_t>(1, kSplitCUs / rows), slots});
+  P.split = (MODE != kModeTopk && !P.direct && !P.force_exact && k != nullptr && (p != nullptr || minp != nullptr) && split > 0)
+                ? (int32_t)split : 0;
+  const unsigned row_grid = (unsigned)(rows * (P.split ? P.split : 1));
   P.out_idx = out_idx;
   P.out_kept = out_kept;
   P.out_mask = out_mask;
@@ -2993,9 +3346,9 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
     if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "nucleus cut kernel launch failed: %s", hipGetErrorString(e));
   }
   if (!P.direct && P.chunks * kW1 > kRW * kGatherB)
-    hipLaunchKernelGGL((ts_row_kernel<MODE, true>), dim3((unsigned)rows), dim3(kRT), 0, s, P);
+    hipLaunchKernelGGL((ts_row_kernel<MODE, true>), dim3(row_grid), dim3(kRT), 0, s, P);
   else
-    hipLaunchKernelGGL((ts_row_kernel<MODE, false>), dim3((unsigned)rows), dim3(kRT), 0, s, P);
+    hipLaunchKernelGGL((ts_row_kernel<MODE, false>), dim3(row_grid), dim3(kRT), 0, s, P);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TS_ERR_LAUNCH, "row kernel launch failed: %s", hipGetErrorString(e));
   return TS_OK;

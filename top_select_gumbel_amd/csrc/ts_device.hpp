@@ -300,13 +300,16 @@ __device__ __forceinline__ float gumbel_from_uniform(float u) {
 // The same value through binary64 (exact: a power-of-two scale, then truncation). Measured
 // faster than the shifts in the rejection kernel's all-token passes, slower elsewhere.
 __device__ __forceinline__ uint64_t mass64_of(float w, int s) { return (uint64_t)ldexp((double)w, s); }
+// Written with selects only: both shifts are formed and one is kept, so a wave never splits.
 __device__ __forceinline__ uint64_t mass32_of(float w, int s) {
   const uint32_t b = __float_as_uint(w);
   const int e = (int)((b >> 23) & 0xFFu);
-  if (e == 0) return 0ull;
   const uint64_t m = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
   const int sh = e - 150 + s;
-  return sh >= 0 ? (m << sh) : (sh > -24 ? (m >> -sh) : 0ull);
+  const uint64_t up = m << (sh & 63);
+  const uint64_t dn = m >> ((-sh) & 63);
+  const uint64_t r = sh >= 0 ? up : (sh > -24 ? dn : 0ull);
+  return e == 0 ? 0ull : r;
 }
 
 
@@ -317,12 +320,14 @@ constexpr double kLog2e = 1.4426950408889634;   // log2(e)
 // z = (x - m) * log2(e) / T is formed in binary64 (x - m exact, c2 = log2(e) / T rounded
 // once), split into integer and fraction, and only 2^fraction is evaluated in fp32.
 // -inf logits (and weights below 2^-200) give 0.
-__device__ __forceinline__ float weight32(uint32_t key, float m, double c2) {
-  const double z = ((double)key2f(key) - (double)m) * c2;   // <= 0
+// The fraction lies in [0, 1), so the hardware base-2 exponential needs no range reduction.
+__device__ __forceinline__ float weightf(float x, float m, double c2) {
+  const double z = ((double)x - (double)m) * c2;   // <= 0
   if (!(z > -200.0)) return 0.0f;
   const double n = floor(z);
-  return ldexpf(exp2f((float)(z - n)), (int)n);
+  return ldexpf(__builtin_amdgcn_exp2f((float)(z - n)), (int)n);
 }
+__device__ __forceinline__ float weight32(uint32_t key, float m, double c2) { return weightf(key2f(key), m, c2); }
 
 // Natural logarithm of a positive normal binary64 z, fp32-accurate (absolute error below
 // 1e-7 for z >= 1): z = f * 2^e with f in [0.5, 1), log z = (e + log2 f) ln 2, log2 f from the
