@@ -2396,8 +2396,10 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   uint64_t* mine = slots + (int64_t)part * 2 * kNucBins;
   static_assert(kNucBins == 2 * kRT, "two bins per thread");
   // The slots are written with device-scope atomic stores, which write through to the point
-  // of coherence of all XCDs, and read with device-scope atomic loads: once every store has
-  // completed (the wait below), the part is published without a cache write-back fence.
+  // of coherence of all XCDs, and read with device-scope atomic loads. Every thread waits for
+  // its stores to complete before the barrier; the counter's fetch-add then releases the part
+  // and, in the last workgroup, acquires the others (one agent-scope fence pair per
+  // workgroup: a fence in every thread costs tens of microseconds in L2 write-backs).
   auto put = [&](uint64_t* a, uint64_t v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   if (binned) {
     const int i = 2 * (int)threadIdx.x;
@@ -2424,7 +2426,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   bar();
-  if (threadIdx.x == 0) sm.res[3] = __hip_atomic_fetch_add(&nr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) sm.res[3] = __hip_atomic_fetch_add(&nr->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
   bar();
   const bool last = sm.res[3] == (uint32_t)(G - 1);
   bar();
