@@ -118,6 +118,34 @@ def test_long_rows_flat_gather_all_entry_points():
     check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, "long rows")
 
 
+def test_million_logit_rows_flat_gather_widest_round():
+    """Rows of 2^20 logits with k = 2048 publish about 9,700 candidates: more than 16 per
+    thread, so the flat gather takes its widest per-thread round (24 items) in the sampling and
+    top-p instantiations too, not only in top-k select."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(4004)
+    rows, v = 2, 1 << 20
+    x = rng.standard_normal((rows, v)).astype(np.float32)
+    x[1] = np.round(x[1], 3)                     # ties at the top-k boundary
+    k = np.array([2048, 2048], np.int32)
+    p = np.array([0.9, 1.0], np.float32)
+    t = np.array([1.0, 0.8], np.float32)
+    seeds = rng.integers(0, 2 ** 64, rows, dtype=np.uint64)
+    banner(f"million-logit rows V={v}: topk")
+    idx, st = ts.ts_topk_select(dev(x), dev(k), 2048)
+    torch.cuda.synchronize()
+    check_topk(x, k, 2048, host(idx), host(st), "million rows")
+    banner(f"million-logit rows V={v}: topp")
+    kept, mask, st2 = ts.ts_topp_mask(dev(x), dev(k), dev(p), dev(t), True)
+    torch.cuda.synchronize()
+    kept = host(kept)
+    check_topp(x, k, p, t, kept, host(mask), host(st2), "million rows")
+    banner(f"million-logit rows V={v}: sample")
+    tok, st3 = ts.ts_sample_rows(dev(x), dev(k), dev(p), dev(t), dev(seeds))
+    torch.cuda.synchronize()
+    check_samples(x, k, p, t, seeds, host(tok), host(st3), kept, "million rows")
+
+
 def test_constant_stretches_uniform_slices():
     """Rows holding stretches of one repeated value (V = 151936: chunks of 8000 logits, wave
     shares of 2000). A wave whose every element is one key publishes a uniform slice (no

@@ -339,12 +339,17 @@ __device__ __forceinline__ double log_fast(double z) {
 }
 
 // ceil(p * Z) for p = fp32 in (0, 1) and a fixed-point total Z: with p = mant * 2^-psh
-// (mant < 2^24) the product is exact in 128 bits.
+// (mant < 2^24, read from p's bits: the significand with its hidden bit, or a subnormal's
+// bits over 2^149) the product is exact in 128 bits. Callers pass workgroup-uniform values;
+// they are moved to scalar registers first, so the integer arithmetic runs once on the scalar
+// unit instead of on every lane.
 __device__ __forceinline__ uint64_t topp_target(float p, uint64_t z) {
-  int pe;
-  const float pf = frexpf(p, &pe);                          // p = pf * 2^pe, pf in [0.5, 1)
-  const uint64_t mant = (uint64_t)ldexpf(pf, 24);
-  const int psh = 24 - pe;                                  // > 24 since p < 1
+  const uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p));
+  z = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(z >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)z);
+  const uint32_t e = (pb >> 23) & 0xFFu;                     // p in (0, 1): e < 127
+  const uint64_t mant = e ? ((pb & 0x7FFFFFu) | 0x800000u) : (pb & 0x7FFFFFu);
+  const int psh = e ? 150 - (int)e : 149;                   // > 24
   const unsigned __int128 prod = (unsigned __int128)mant * z;
   return psh >= 128 ? (prod != 0 ? 1ull : 0ull)
                     : (uint64_t)((prod + (((unsigned __int128)1 << psh) - 1)) >> psh);
