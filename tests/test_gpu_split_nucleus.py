@@ -113,3 +113,24 @@ def test_split_nucleus_counted_twice_in_a_row():
             ref = tok
         assert np.array_equal(tok[:7], ref[:7]) if rows == 7 else np.array_equal(tok, ref)
         assert (host(st) == 0).all()
+
+
+def test_split_nucleus_decode_rows_as_benched():
+    """The decode rows with a top-k array of k = V (64 x 151936: 4 parts per row), as the
+    decode_topp_only bench times them: the same bytes as the nucleus passes and the
+    row-streaming path, and every row against the oracle."""
+    from top_select_gumbel_amd import workloads as wl
+    b = wl.decode_topp_only()
+    x, k, p, t, seeds = b.logits, b.k, b.p, b.t, b.seeds
+    xs, kd, pd, td, sd = dev(x), d(k, np.int32), d(p, np.float32), d(t, np.float32), dev(seeds)
+    label = "split nucleus decode 64x151936"
+    banner(f"{label}: topp")
+    outs = three_ways(lambda use_k: ts.ts_topp_mask(xs, kd if use_k else None, pd, td, True))
+    same(outs, "topp mask")
+    kept, mask, st = outs[0]
+    op.check_topp(x, k, p, t, kept, mask, st, label)
+    banner(f"{label}: sample")
+    outs = three_ways(lambda use_k: ts.ts_sample_rows(xs, kd if use_k else None, pd, td, sd))
+    same(outs, "sample")
+    tok, st2 = outs[0]
+    op.check_samples(x, k, p, t, seeds, tok, st2, kept, label)
