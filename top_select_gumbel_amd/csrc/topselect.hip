@@ -2319,20 +2319,21 @@ __device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32
 // workgroups do not run for them). The row kernel runs P.split workgroups per row; each takes
 // a contiguous part of the row and, with the row maximum m known from the wave summaries:
 //  - bins every token's exact fixed-point mass by value in the window below m (nuc_bin; bin 0
-//    below the window, summed in registers) and adds the part's bins to the row's histogram;
+//    below the window, summed in registers);
 //  - sampling: draws the Gumbel score of every token of the window that min-p keeps (one
 //    Philox block per quad) and keeps the best per bin (p == 1: one best for the row), since
 //    the kept set is every bin above the cut plus a prefix of the cut bin, whichever bin that
-//    turns out to be.
-// Each part stores its bins (plain stores) into its own slot in the row's candidate area, which
-// rows of this kind leave unused. The last workgroup of the row to finish its part (a counter;
-// no workgroup ever waits for another) then sums the slots, finds the cut bin where the mass from the top reaches ceil(p * Z), lists that
-// bin's tokens in LDS from one compare-only read of the row (top-p masks: also marks the
-// tokens above the cut), and takes the exact cut inside it with the same fixed-point select
-// as the exact path. The sampled token is the best of the bins above the cut and of the
-// selected members of the cut bin. Returns false only in the finishing workgroup, when the cut
-// bin holds more tokens than the LDS list (the caller then takes the row-streaming path, which
-// writes the same mask bytes).
+//    turns out to be;
+//  - stores its bins into its own slot in the row's candidate area (unused by rows of this
+//    kind) and counts itself done on the row's counter.
+// The workgroup that counts last (no workgroup ever waits for another) sums the slots, finds
+// the cut bin where the mass from the top reaches ceil(p * Z), lists that bin's tokens in LDS
+// from one compare-only read of the row (top-p masks: also marks the tokens above the cut),
+// and takes the exact cut inside it with the same fixed-point select as the exact path. The
+// sampled token is the best of the bins above the cut and of the selected members of the cut
+// bin. Returns false only in the finishing workgroup, when the cut bin holds more tokens than
+// the LDS list (the caller then takes the row-streaming path, which writes the same mask
+// bytes).
 template <int MODE>
 __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, int r, uint32_t kmax,
                                             uint64_t seed, Smem& sm, double lse, int part) {
