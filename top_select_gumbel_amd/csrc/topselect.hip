@@ -2395,7 +2395,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
     block_sum2_u64<kRW>(z0, zl, sm.red64);   // its barriers also complete the LDS atomics
   }
   uint64_t* mine = slots + (int64_t)part * 2 * kNucBins;
-  static_assert(kNucBins == 2 * kRT, "two bins per thread");
+  static_assert(kNucBins % (2 * kRT) == 0, "bins in pairs per thread");
   // The slots are written with device-scope atomic stores, which write through to the point
   // of coherence of all XCDs, and read with device-scope atomic loads. Every thread waits for
   // its stores to complete before the barrier; the counter's fetch-add then releases the part
@@ -2403,16 +2403,17 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   // workgroup: a fence in every thread costs tens of microseconds in L2 write-backs).
   auto put = [&](uint64_t* a, uint64_t v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   if (binned) {
-    const int i = 2 * (int)threadIdx.x;
-    put(mine + i, sm.mhi[i] + (threadIdx.x == 0 ? z0 : 0ull));
-    put(mine + i + 1, sm.mhi[i + 1]);
-    sm.mhi[i] = 0;
-    sm.mhi[i + 1] = 0;
-    if (MODE == kModeSample) {
-      put(mine + kNucBins + i, bbest[i]);
-      put(mine + kNucBins + i + 1, bbest[i + 1]);
-      bbest[i] = 0;
-      bbest[i + 1] = 0;
+    for (int i = 2 * (int)threadIdx.x; i < kNucBins; i += 2 * kRT) {
+      put(mine + i, sm.mhi[i] + (i == 0 ? z0 : 0ull));
+      put(mine + i + 1, sm.mhi[i + 1]);
+      sm.mhi[i] = 0;
+      sm.mhi[i + 1] = 0;
+      if (MODE == kModeSample) {
+        put(mine + kNucBins + i, bbest[i]);
+        put(mine + kNucBins + i + 1, bbest[i + 1]);
+        bbest[i] = 0;
+        bbest[i + 1] = 0;
+      }
     }
   } else if (MODE == kModeSample) {
     uint32_t hi = (uint32_t)(best >> 32);
@@ -2437,15 +2438,17 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   int cut = -1;                 // bins above it are kept whole; p == 1: every token
   uint64_t target = 0, ma = 0;
   if (binned) {
-    const int i = 2 * (int)threadIdx.x;
-    uint64_t m0 = 0, m1 = 0, zl = 0;
-    for (int g = 0; g < G; ++g) {
-      m0 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      m1 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t zh = 0, zl = 0;
+    for (int i = 2 * (int)threadIdx.x; i < kNucBins; i += 2 * kRT) {
+      uint64_t m0 = 0, m1 = 0;
+      for (int g = 0; g < G; ++g) {
+        m0 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        m1 += __hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sm.mhi[i] = m0;
+      sm.mhi[i + 1] = m1;
+      zh += m0 + m1;
     }
-    sm.mhi[i] = m0;
-    sm.mhi[i + 1] = m1;
-    uint64_t zh = m0 + m1;
     block_sum2_u64<kRW>(zh, zl, sm.red64);
     target = topp_target(rp.p, zh);
     search_mass(sm, target, 0ull);           // also clears the histograms for the exact cut
