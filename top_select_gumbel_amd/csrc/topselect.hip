@@ -2078,7 +2078,7 @@ struct SmemC {
   uint32_t red[4 * kW1];
   uint64_t red64[2 * kW1];
   uint32_t res[2];
-  uint32_t mkey[kW1][256];     // a wave's members of one load slot (compacted for the noise)
+  uint32_t mkey[kW1][256];     // a wave's kept tokens, compacted across load slots for the noise
   uint32_t mid[kW1][256];
 };
 
@@ -2186,6 +2186,24 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
   uint64_t best = 0;
   uint64_t n_up = 0, k_up = 0;   // this thread's tokens above the cut bin, and those min-p keeps
   const int w = wave(), l = lane();
+  // Sampling: the kept tokens are scattered over the wave's lanes and slots. They are
+  // compacted into the wave's LDS buffer across slots (flushed when the next slot would
+  // overflow it, and at the end), so the generator and the noise run on full lanes, once per
+  // member: not once per quad of every lane whenever any lane has one, nor once per slot.
+  constexpr uint32_t kMemCap = sizeof(sm.mkey[0]) / sizeof(sm.mkey[0][0]);
+  uint32_t nmem = 0;   // wave-uniform
+  auto flush = [&]() {
+    if (nmem) {
+      wave_lds_sync();
+      for (uint32_t j = (uint32_t)l; j < nmem; j += 64) {
+        const uint32_t key = sm.mkey[w][j], id = sm.mid[w][j];
+        const float sc = gumbel_score(key, id, m, rp.t, (uint32_t)r, k0, k1);
+        best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~id);
+      }
+      wave_lds_sync();
+      nmem = 0;
+    }
+  };
 #pragma unroll
   for (int s = 0; s < kQ; ++s) {
     const uint32_t id0 = (uint32_t)(c0 + 4 * ((int)threadIdx.x + s * kT1));
@@ -2206,28 +2224,22 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
       }
     }
     if (MODE == kModeSample) {
-      // members are scattered over the wave's lanes: compact them first, so that the
-      // generator and the noise run on full lanes (once per member, not once per quad of
-      // every lane whenever any lane has one)
-      uint32_t nmem = 0;
+      uint64_t bal[4];
+      uint32_t cnt = 0;   // this slot's members over the wave: at most 256 = kMemCap
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint64_t bal = __ballot(mem[e]);
+        bal[e] = __ballot(mem[e]);
+        cnt += (uint32_t)__popcll(bal[e]);
+      }
+      if (nmem + cnt > kMemCap) flush();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
         if (mem[e]) {
-          const uint32_t pos = nmem + mbcnt(bal);
+          const uint32_t pos = nmem + mbcnt(bal[e]);
           sm.mkey[w][pos] = f2key(elem(s, e));
           sm.mid[w][pos] = id0 + (uint32_t)e;
         }
-        nmem += (uint32_t)__popcll(bal);
-      }
-      if (nmem) {
-        wave_lds_sync();
-        for (uint32_t j = (uint32_t)l; j < nmem; j += 64) {
-          const uint32_t key = sm.mkey[w][j], id = sm.mid[w][j];
-          const float sc = gumbel_score(key, id, m, rp.t, (uint32_t)r, k0, k1);
-          best = max(best, ((uint64_t)f2key(sc) << 32) | (uint32_t)~id);
-        }
-        wave_lds_sync();
+        nmem += (uint32_t)__popcll(bal[e]);
       }
     }
     if (MODE == kModeTopp && mrow) {
@@ -2236,6 +2248,7 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
         if (mem[e]) mrow[id0 - c0 + e] = 1;
     }
   }
+  if (MODE == kModeSample) flush();
   // the workgroup's tokens above the cut bin (and those min-p keeps): one atomic each
   block_sum2_u64<kW1>(n_up, k_up, sm.red64);
   if (threadIdx.x == 0 && n_up) {
