@@ -2052,7 +2052,7 @@ __global__ __launch_bounds__(kNT) void ts_nucleus_kernel(Params P) {
   uint64_t z0m = 0;
   chunk_visit<kNT>(row, n, [&](float x, uint32_t) {
     const uint32_t bin = nuc_bin(x, nb);
-    const uint64_t q = mass32_of(weight32(f2key(x), m, c2), S);
+    const uint64_t q = massf(x, m, c2, S);
     if (bin == 0u) z0m += q;
     else if (q) atomicAdd((unsigned long long*)&sm.mass[bin], (unsigned long long)q);
   });
@@ -2382,7 +2382,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
     for (int e = 0; e < 4; ++e) {
       bin[e] = binned ? nuc_bin(xs[e], nb) : 1u;
       if (binned && live) {
-        const uint64_t q64 = mass32_of(weightf(xs[e], m, c2), S);   // 0 for the -inf past the row end
+        const uint64_t q64 = massf(xs[e], m, c2, S);   // 0 for the -inf past the row end
         if (bin[e] == 0u) z0 += q64;
         else if (q64) atomicAdd((unsigned long long*)&sm.mhi[bin[e]], (unsigned long long)q64);
       }

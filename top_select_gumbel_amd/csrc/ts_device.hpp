@@ -329,6 +329,23 @@ __device__ __forceinline__ float weightf(float x, float m, double c2) {
 }
 __device__ __forceinline__ float weight32(uint32_t key, float m, double c2) { return weightf(key2f(key), m, c2); }
 
+// mass32_of(weightf(x, m, c2), s) in one step: the power of two of the fraction is read as a
+// 24-bit significand and shifted once by the exponent's integer part, instead of being scaled
+// into a float and taken apart again. Equal bit for bit: a normal weight has that significand
+// and exponent; a weight the scaling would make subnormal or zero (exponent below -126) is
+// shifted out to 0 here too, as s <= 63.
+__device__ __forceinline__ uint64_t massf(float x, float m, double c2, int s) {
+  const double z = ((double)x - (double)m) * c2;   // <= 0
+  if (!(z > -200.0)) return 0ull;
+  const double n = floor(z);
+  const uint32_t b = __float_as_uint(__builtin_amdgcn_exp2f((float)(z - n)));   // in [1, 2]
+  const uint64_t mant = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+  const int sh = (int)n + (int)(b >> 23) - 150 + s;
+  const uint64_t up = mant << (sh & 63);
+  const uint64_t dn = mant >> ((-sh) & 63);
+  return sh >= 0 ? up : (sh > -24 ? dn : 0ull);
+}
+
 // Natural logarithm of a positive normal binary64 z, fp32-accurate (absolute error below
 // 1e-7 for z >= 1): z = f * 2^e with f in [0.5, 1), log z = (e + log2 f) ln 2, log2 f from the
 // hardware base-2 logarithm of fp32(f).
