@@ -1,6 +1,6 @@
 """Shared helpers for the GPU parity tests: device transfer and the matching rules.
 
-Matching rules (batched sampling the benchmark spec):
+Matching rules for batched top-k, top-p and sampling:
   * top-k: out_idx bytes equal the oracle's for every row;
   * top-p: kept counts equal the oracle's (rows whose binary64 boundary the oracle cannot
     certify are exempt from equality but not from the mass bound); the kept set is a canonical
