@@ -196,7 +196,7 @@ struct Smem {
   uint32_t kkey[kFastK];       // the kept set P, compacted for the Gumbel draws
   uint32_t kidx[kFastK];
   uint32_t segoff[kMaxSeg + 1];
-  uint32_t red[4 * kRW];
+  uint32_t red[5 * kRW];
   uint64_t red64[2 * kRW];
   float reds[kRW];
   int32_t redi[kRW];
@@ -2754,6 +2754,9 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   uint32_t flags = 0, kmax = 0, thr_max = 0, cmin = 0xFFFFFFFFu;
   uint32_t kw0 = kKeyNegInf;   // the maximum key of this thread's first slice
   double ws0 = 0.0;            // and its exponential sum (sampling with logprobs)
+  uint32_t cnt0 = 0;           // and its candidate count
+  // At most one slice per thread: the slice offsets come with the summaries' reduction.
+  const bool one_slice = !P.direct && nseg <= kRT;
   RowPlan rp;
   if (P.direct) {
     // The whole row is the candidate set: its keys and ids go straight to LDS (no stream
@@ -2778,12 +2781,15 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     if (MODE == kModeSample && P.wsum && (int)threadIdx.x < nseg) ws0 = P.wsum[(int64_t)r * nseg + threadIdx.x];
     for (int i = threadIdx.x; i < nseg; i += kRT) {
       const WaveInfo wi = inf[i];
-      if (i == (int)threadIdx.x) kw0 = wi.kmax;
+      if (i == (int)threadIdx.x) {
+        kw0 = wi.kmax;
+        cnt0 = wi.count;
+      }
       flags |= wi.flags;
       kmax = max(kmax, wi.kmax);
       thr_max = max(thr_max, wi.thr);
       cmin = min(cmin, wi.thr);
-      if (i < kMaxSeg) sm.segoff[i] = wi.count;
+      if (!one_slice && i < kMaxSeg) sm.segoff[i] = wi.count;
     }
     rp = plan_row(P, MODE, r);
   }
@@ -2795,7 +2801,15 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
   }
   // kmax, thr_max: maxima; cmin: every candidate key is >= the smallest threshold
-  block_reduce4<kRW>(kmax, thr_max, cmin, flags, sm.red);
+  uint32_t seg_total = 0;
+  if (one_slice) {
+    uint32_t excl;
+    block_reduce4_scan<kRW>(kmax, thr_max, cmin, flags, cnt0, excl, seg_total, sm.red);
+    if ((int)threadIdx.x < nseg) sm.segoff[threadIdx.x] = excl;   // read after the gathers' barrier
+    if (threadIdx.x == 0) sm.segoff[nseg] = seg_total;
+  } else {
+    block_reduce4<kRW>(kmax, thr_max, cmin, flags, sm.red);
+  }
   const bool nan = (flags & kFlagNan) != 0;
   int st = TS_ROW_OK;
   if (MODE == kModeTopk) {
@@ -2936,23 +2950,25 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     }
   } else if (path == kPathCand && nseg <= kMaxSeg) {
     const uint32_t ke = (uint32_t)rp.k_eff;
-    // exclusive prefix of the slice counts (kSegPT consecutive slices per thread): the
-    // candidates' flat, id-ordered index space
-    const int s0 = kSegPT * (int)threadIdx.x;
-    uint32_t cs[kSegPT], csum = 0;
+    // exclusive prefix of the slice counts: the candidates' flat, id-ordered index space
+    // (with one slice per thread it came with the summaries' reduction)
+    uint32_t total = seg_total;
+    if (!one_slice) {
+      const int s0 = kSegPT * (int)threadIdx.x;   // kSegPT consecutive slices per thread
+      uint32_t cs[kSegPT], csum = 0;
 #pragma unroll
-    for (int q = 0; q < kSegPT; ++q) {
-      cs[q] = s0 + q < nseg ? sm.segoff[s0 + q] : 0u;
-      csum += cs[q];
-    }
-    uint32_t total;
-    uint32_t off = block_excl_scan<kRW>(csum, sm.red, total);   // barrier before the writes
+      for (int q = 0; q < kSegPT; ++q) {
+        cs[q] = s0 + q < nseg ? sm.segoff[s0 + q] : 0u;
+        csum += cs[q];
+      }
+      uint32_t off = block_excl_scan<kRW>(csum, sm.red, total);   // barrier before the writes
 #pragma unroll
-    for (int q = 0; q < kSegPT; ++q) {
-      if (s0 + q < nseg) sm.segoff[s0 + q] = off;
-      off += cs[q];
+      for (int q = 0; q < kSegPT; ++q) {
+        if (s0 + q < nseg) sm.segoff[s0 + q] = off;
+        off += cs[q];
+      }
+      if (threadIdx.x == 0) sm.segoff[nseg] = total;
     }
-    if (threadIdx.x == 0) sm.segoff[nseg] = total;
     // Wave w published the elements >= its threshold (at most the cap of them when it
     // overflowed): at least `total` elements are >= cmin, so the k-th key is >= cmin (used
     // only when a top-k select runs, k < V).

@@ -178,6 +178,39 @@ __device__ __forceinline__ void block_reduce4(uint32_t& mx1, uint32_t& mx2, uint
   }
   bar();
 }
+// block_reduce4 together with an exclusive prefix of v over the threads in order (excl) and
+// its total: one exchange through LDS for all of them (red: 5 * NW).
+template <int NW>
+__device__ __forceinline__ void block_reduce4_scan(uint32_t& mx1, uint32_t& mx2, uint32_t& mn, uint32_t& orv,
+                                                   uint32_t v, uint32_t& excl, uint32_t& total, uint32_t* red) {
+  mx1 = wave_max(mx1);
+  mx2 = wave_max(mx2);
+  mn = wave_min(mn);
+  orv = wave_or(orv);
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane() == 0) {
+    red[wave()] = mx1;
+    red[NW + wave()] = mx2;
+    red[2 * NW + wave()] = mn;
+    red[3 * NW + wave()] = orv;
+  }
+  if (lane() == 63) red[4 * NW + wave()] = incl;
+  bar();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mx1 = max(mx1, red[w]);
+    mx2 = max(mx2, red[NW + w]);
+    mn = min(mn, red[2 * NW + w]);
+    orv |= red[3 * NW + w];
+    const uint32_t t = red[4 * NW + w];
+    base += (w < wave()) ? t : 0u;
+    tot += t;
+  }
+  excl = base + incl - v;
+  total = tot;
+  bar();
+}
 // Sums of two 64-bit values at once (red: 2 * NW).
 template <int NW>
 __device__ __forceinline__ void block_sum2_u64(uint64_t& a, uint64_t& b, uint64_t* red) {
