@@ -328,7 +328,10 @@ __device__ __forceinline__ void search_count(Smem& sm, uint32_t need) {
 // fixed-point sums (one 64-bit word floor(w * 2^S) per weight). Writes res[0] = b,
 // res[1] = count above b, res[2] = count in b, res64[0] = ma + mass above b, res64[1] = mass
 // of b. The caller guarantees that ma plus the whole histogram reaches the target.
-__device__ __forceinline__ void search_mass(Smem& sm, uint64_t target_fx, uint64_t ma) {
+// With zp > 0 the target is ceil(zp * Z), Z being the whole histogram's mass (the caller's
+// first pass weighed every item into it): it is computed here from the waves' totals, after the
+// exchange this search needs anyway, and left in res64[2].
+__device__ __forceinline__ void search_mass(Smem& sm, uint64_t target_fx, uint64_t ma, float zp = 0.0f) {
   const int t = threadIdx.x;
   uint32_t c[kBPT];
   uint64_t mh[kBPT];
@@ -352,12 +355,17 @@ __device__ __forceinline__ void search_mass(Smem& sm, uint64_t target_fx, uint64
   }
   bar();
   uint32_t ac = 0;
-  uint64_t ah = 0;
+  uint64_t ah = 0, z = 0;
 #pragma unroll
   for (int w = 0; w < kRW; ++w) {
     const bool up = w > wave();
     ac += up ? sm.red[w] : 0u;
     ah += up ? sm.red64[w] : 0ull;
+    z += sm.red64[w];
+  }
+  if (zp > 0.0f) {
+    target_fx = topp_target(zp, z);
+    if (threadIdx.x == 0) sm.res64[2] = target_fx;
   }
   uint32_t xc = ac + sc - lc;
   uint64_t xh = ma + ah + sh - lh;
@@ -613,7 +621,8 @@ template <bool COLLECT = false, class KVis, class WMass>
 __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass, uint64_t target_fx,
                                            uint32_t n_in_play, uint32_t hi_key, uint32_t lo_key,
                                            uint32_t idx_lo, uint32_t idx_hi, Smem& sm, uint32_t& kept,
-                                           bool prebuilt = false, uint64_t ma0 = 0, uint32_t n_above0 = 0) {
+                                           bool prebuilt = false, uint64_t ma0 = 0, uint32_t n_above0 = 0,
+                                           float zp = 0.0f) {
   int lo = (hi_key == lo_key) ? 0 : 32 - __clz((int)(hi_key ^ lo_key));
   uint32_t prefix = shr(hi_key, lo);
   uint32_t n_above = n_above0, tie_cnt = n_in_play;
@@ -637,7 +646,11 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
       bar();
     }
     counted = false;
-    search_mass(sm, target_fx, ma);
+    search_mass(sm, target_fx, ma, zp);
+    if (zp > 0.0f) {   // the first search took the target from the prebuilt histogram
+      target_fx = sm.res64[2];
+      zp = 0.0f;
+    }
     const uint32_t bin = sm.res[0];
     n_above += sm.res[1];
     tie_cnt = sm.res[2];
@@ -1493,11 +1506,18 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
         }
       }
     }
-    block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the atomics and stores
     // [TOPP] reference steps 4-5 in exact fixed point: keep the shortest prefix whose mass is
-    // >= p * Z, i.e. >= ceil(p * Z) since masses are integers.
-    const uint64_t target_fx = topp_target(rp.p, zh);
-    sp = select_mass(kvis, wmass, target_fx, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, pre);
+    // >= p * Z, i.e. >= ceil(p * Z) since masses are integers. With the first pass prebuilt,
+    // Z is the histogram's total and the first search computes the target from it; else a
+    // block sum of the items' masses gives it.
+    if (pre) {
+      bar();   // completes the atomics and the scores' stores
+      sp = select_mass(kvis, wmass, 0ull, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, true, 0ull, 0u, rp.p);
+    } else {
+      block_sum2_u64<kRW>(zh, zl, sm.red64);   // its barriers also complete the stores
+      const uint64_t target_fx = topp_target(rp.p, zh);
+      sp = select_mass(kvis, wmass, target_fx, nk, kmax, klo, 0u, (uint32_t)(P.V - 1), sm, kept, false);
+    }
   }
   // min-p after top-p: the members of P whose weight is >= min_p (the maximum has weight 1),
   // again a canonical prefix ([LOGP] relay order temperature -> top-k -> top-p -> min-p).
