@@ -5,7 +5,10 @@ their workspace in the library's static device scratch. Its results must equal t
 ts_sample_rows (which takes a caller workspace) byte for byte, on two calls in a row on the
 same GPU, the second with a smaller batch, so the second call runs over the first one's
 leftovers in the shared scratch. Both batches include tie-heavy rows whose waves publish more
-candidates than the allocation-free slices hold, so those rows take the exact path there.
+candidates than the allocation-free slices hold, so those rows take the exact path there, and
+rows whose top-k entry reaches the vocabulary, which take the split nucleus (its parts' slots
+live in the candidate area, so the smaller allocation-free slices give the second batch fewer
+parts per row: 3 against 8).
 """
 import ctypes
 
@@ -26,7 +29,10 @@ def batch(rows, vocab, seed):
     x[2, : vocab // 2] = np.float32(7.0)               # half the row tied at the top
     k = b.k.copy()
     k[1], k[2] = 700, 1500
-    return x, k, b.p, b.t, b.seeds
+    k[3], k[4] = vocab, vocab + 5                      # top-k off by value: the split nucleus,
+    p = b.p.copy()                                     # over as many parts as each scratch holds
+    p[4] = np.float32(0.3)
+    return x, k, p, b.t, b.seeds
 
 
 def run_both(x, k, p, t, seeds):
