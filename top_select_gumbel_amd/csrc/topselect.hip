@@ -800,16 +800,13 @@ __device__ __forceinline__ void kvis_i(uint32_t n, F f, Smem& sm) {
 
 // Append the items of [0, n) of (ka, ia) that satisfy `mem` to (dkey, didx), in any order:
 // per round, a wave scan of the per-lane counts and one LDS atomic per wave reserve room.
-// Returns the count (entries past `cap` are dropped). Ends with a barrier. Successive calls
-// alternate between two counters (slot), so a call never resets a counter that other
-// threads may still be reading.
+// Returns the count (entries past `cap` are dropped). Ends with a barrier. The slot's counter
+// must be zero on entry: the row kernel clears it at its start, and a workgroup compacts once.
 template <class Mem>
 __device__ __forceinline__ uint32_t append_members(const uint32_t* ka, const uint32_t* ia, uint32_t n,
                                                    const Mem& mem, uint32_t* dkey, uint32_t* didx,
                                                    uint32_t cap, int slot, Smem& sm) {
   uint32_t* counter = &sm.kcount[slot];
-  if (threadIdx.x == 0) *counter = 0;
-  bar();
   for (uint32_t base = threadIdx.x - (uint32_t)lane(); base < n; base += kRT * kVisU) {
     // wave-uniform loop: base is the wave's first item of the round
     uint32_t k[kVisU], x[kVisU];
@@ -1562,7 +1559,7 @@ __device__ __forceinline__ void finish_cand(const Params& P, const RowPlan& rp, 
         if (sc > bs || (sc == bs && (int32_t)idx < bi)) { bs = sc; bi = (int32_t)idx; }
       }
     }
-    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
+    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi, nullptr, true);
     if (threadIdx.x == 0) {
       P.out_token[r] = tok;
       put_logp(P, r, tok, t, lse);
@@ -1784,7 +1781,7 @@ __device__ __forceinline__ void row_stream(const Params& P, const RowPlan& rp, i
       for (int u = 0; u < kPer; ++u) cur[u] = nxt[u];
       bar();
     }
-    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
+    const int32_t tok = block_argmax<kRW>(bs, bi, sm.reds, sm.redi, nullptr, true);
     if (threadIdx.x == 0) {
       P.out_token[r] = tok;
       put_logp(P, r, tok, t, lse);
@@ -2814,8 +2811,12 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
     rp = plan_row(P, MODE, r);
   }
   const uint64_t seed = (MODE == kModeSample) ? P.seed[r] : 0ull;
-  // zero the histograms (each select leaves them zero again) and the small-bin counter
-  if (threadIdx.x == 0) sm.bcount = 0;
+  // zero the histograms (each select leaves them zero again), the small-bin counter and the
+  // compaction counter (one compaction per workgroup)
+  if (threadIdx.x == 0) {
+    sm.bcount = 0;
+    sm.kcount[0] = 0;
+  }
   for (int i = threadIdx.x; i < kDBins / 4; i += kRT) reinterpret_cast<uint4*>(sm.hist)[i] = make_uint4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kDBins / 2; i += kRT) {
     reinterpret_cast<uint4*>(sm.mhi)[i] = make_uint4(0, 0, 0, 0);
@@ -2937,7 +2938,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
           if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
         }
       }
-      bi = block_argmax<kRW>(bs, bi, sm.reds, sm.redi);
+      bi = block_argmax<kRW>(bs, bi, sm.reds, sm.redi, nullptr, true);
       if (threadIdx.x == 0) {
         P.out_token[r] = bi;
         put_logp(P, r, bi, rp.t, lse);

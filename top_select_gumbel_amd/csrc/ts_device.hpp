@@ -266,8 +266,9 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 // finite one; scores are never NaN.
 template <int NW>
+// `last`: the workgroup's final use of reds / redi, so no barrier needs to protect their reuse.
 __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds, int32_t* redi,
-                                                float* best_s = nullptr) {
+                                                float* best_s = nullptr, bool last = false) {
   wave_argmax(s, id);
   if (lane() == 0) { reds[wave()] = s; redi[wave()] = id; }
   bar();
@@ -277,7 +278,7 @@ __device__ __forceinline__ int32_t block_argmax(float s, int32_t id, float* reds
   uint32_t bi = 0xFFFFFFFFu;
 #pragma unroll
   for (int w = 0; w < NW; ++w) bi = (f2key(reds[w]) == km) ? min(bi, (uint32_t)redi[w]) : bi;
-  bar();
+  if (!last) bar();
   if (best_s) *best_s = key2f(km);
   return (int32_t)bi;
 }
