@@ -2826,8 +2826,9 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
   if (one_slice) {
     uint32_t excl;
     block_reduce4_scan<kRW>(kmax, thr_max, cmin, flags, cnt0, excl, seg_total, sm.red);
-    if ((int)threadIdx.x < nseg) sm.segoff[threadIdx.x] = excl;   // read after the gathers' barrier
+    if ((int)threadIdx.x < nseg) sm.segoff[threadIdx.x] = excl;
     if (threadIdx.x == 0) sm.segoff[nseg] = seg_total;
+    bar();   // the offsets are visible to the gathers, and `red` is free again
   } else {
     block_reduce4<kRW>(kmax, thr_max, cmin, flags, sm.red);
   }
@@ -3007,7 +3008,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
         lo_key = kmax;
       }
     } else if (fast && total <= (uint32_t)kLdsCand) {
-      bar();
+      if (!one_slice) bar();   // the offsets just written (with one slice per thread, already)
       // The top-k select's first pass is counted while the candidates are written to LDS:
       // every candidate key lies in [cmin, kmax], so its digit needs no prefix test.
       const Digit g0 = first_digit(kmax, cmin);

@@ -179,7 +179,8 @@ __device__ __forceinline__ void block_reduce4(uint32_t& mx1, uint32_t& mx2, uint
   bar();
 }
 // block_reduce4 together with an exclusive prefix of v over the threads in order (excl) and
-// its total: one exchange through LDS for all of them (red: 5 * NW).
+// its total: one exchange through LDS for all of them (red: 5 * NW). Ends without the
+// barrier that protects `red`: the caller places it (after its own LDS writes).
 template <int NW>
 __device__ __forceinline__ void block_reduce4_scan(uint32_t& mx1, uint32_t& mx2, uint32_t& mn, uint32_t& orv,
                                                    uint32_t v, uint32_t& excl, uint32_t& total, uint32_t* red) {
@@ -209,7 +210,6 @@ __device__ __forceinline__ void block_reduce4_scan(uint32_t& mx1, uint32_t& mx2,
   }
   excl = base + incl - v;
   total = tot;
-  bar();
 }
 // Sums of two 64-bit values at once (red: 2 * NW).
 template <int NW>
