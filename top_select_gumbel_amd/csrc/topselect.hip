@@ -131,6 +131,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // lives in the row's candidate slices, which nucleus rows leave unused).
 constexpr int kSplitCUs = 256;   // row-kernel workgroups that fill the chip (one per CU: its LDS)
 constexpr int kNucBins = 1024;   // nucleus bins (value-linear window below the maximum, and bin 0)
+constexpr int kCodeCap = 4096;   // split nucleus: tokens sharing the cut bin's code, listed at most
+constexpr int kCodePer = kCodeCap / kRT;
 struct NucRow {
   uint64_t mass[kNucBins];     // exact fixed-point mass per bin
   uint64_t best;               // best (ordered score << 32 | ~id) of the kept tokens above the cut bin
@@ -2282,22 +2284,22 @@ __global__ __launch_bounds__(kT1) void ts_nucleus_cut_kernel(Params P) {
 }
 
 // f(v, q, live) for the quads q in [qa, qb) of a row of V elements (elements past V read as
-// -inf), in rounds of 8 quads per thread: quads base + u * kRT + tid, u < 8, with the round
+// -inf), in rounds of U quads per thread: quads base + u * kRT + tid, u < U, with the round
 // index uniform over the workgroup so that f may use wave-wide operations (every lane calls it
 // each round; `live` tells whether its quad exists). An aligned row takes 16-byte loads of its
 // whole quads, the next round's issued before this round is visited (indexes clamped into the
 // row, so every load is in bounds; quads past the range are replaced by -inf with selects, so
 // that no other load stands between a round's loads and their use), then a partial last quad
 // in a round of its own by element loads; an unaligned row takes element loads.
-template <class F>
+template <int U = 8, class F>
 __device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32_t qa, uint32_t qb, F f) {
-  constexpr uint32_t kStep = kRT * 8;
+  constexpr uint32_t kStep = kRT * U;
   const uint32_t nfull = V >> 2;
   auto slow = [&](uint32_t a, uint32_t b) {
     for (uint32_t base = a; base < b; base += kStep) {
-      float4 v[8];
+      float4 v[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < U; ++u) {
         const uint32_t q = base + u * kRT + threadIdx.x;
         v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         if (q < b) {
@@ -2308,7 +2310,7 @@ __device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32
         }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < U; ++u) {
         const uint32_t q = base + u * kRT + threadIdx.x;
         f(v[u], q, q < b);
       }
@@ -2320,18 +2322,18 @@ __device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32
   }
   const float4* row4 = reinterpret_cast<const float4*>(row);
   const uint32_t qe = min(qb, nfull);       // the range's whole quads end here
-  auto load = [&](float4 (&v)[8], uint32_t base) {
+  auto load = [&](float4 (&v)[U], uint32_t base) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = row4[min(base + u * kRT + threadIdx.x, nfull - 1u)];
+    for (int u = 0; u < U; ++u) v[u] = row4[min(base + u * kRT + threadIdx.x, nfull - 1u)];
   };
-  float4 v[8];
+  float4 v[U];
   if (qa < qe) load(v, qa);
   for (uint32_t base = qa; base < qe; base += kStep) {
-    float4 nx[8];
+    float4 nx[U];
     load(nx, base + kStep);          // unconditional (clamped), so the waits below count it
     asm volatile("" ::: "memory");   // keep the next round's loads issued ahead of this round's work
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t q = base + u * kRT + threadIdx.x;
       const bool in = q < qe;
       const float4 w = make_float4(in ? v[u].x : -INFINITY, in ? v[u].y : -INFINITY, in ? v[u].z : -INFINITY,
@@ -2339,9 +2341,31 @@ __device__ __forceinline__ void visit_quads(const float* row, uint32_t V, uint32
       f(w, q, in);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = nx[u];
+    for (int u = 0; u < U; ++u) v[u] = nx[u];
   }
   if (qb > qe && qb > qa) slow(max(qa, qe), qb);   // the partial last quad
+}
+
+// The largest of each of two 64-bit values over the row workgroup (red: 2 * kRW words).
+__device__ __forceinline__ void block_max2_u64(uint64_t& a, uint64_t& b, uint64_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a = max(a, (uint64_t)__shfl_xor((unsigned long long)a, o));
+    b = max(b, (uint64_t)__shfl_xor((unsigned long long)b, o));
+  }
+  if (lane() == 0) {
+    red[wave()] = a;
+    red[kRW + wave()] = b;
+  }
+  bar();
+  a = 0;
+  b = 0;
+#pragma unroll
+  for (int w = 0; w < kRW; ++w) {
+    a = max(a, red[w]);
+    b = max(b, red[kRW + w]);
+  }
+  bar();
 }
 
 // Top-p (and min-p after it) over whole rows whose k reaches the row length, in calls with a
@@ -2387,6 +2411,11 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   const uint32_t per = (nq + (uint32_t)G - 1) / (uint32_t)G;
   const uint32_t qa = min(nq, (uint32_t)part * per), qb = min(nq, qa + per);
   uint64_t* bbest = sm.mhi + kNucBins;      // the upper half of the mass histogram (zero)
+  // Sampling: every part also stores one byte per token, its bin / 4 (0 for bins 0-3 and past the
+  // row), in one word per quad after the parts' slots, so that the finishing workgroup can find
+  // the cut bin's tokens without reading the row's values (a quarter of the bytes).
+  uint32_t* const codes = reinterpret_cast<uint32_t*>(slots + (int64_t)G * 2 * kNucBins);
+  const bool coded = MODE == kModeSample && binned;
 
   // ---- this workgroup's part: masses by bin, and the best score per bin
   uint64_t z0 = 0, best = 0;
@@ -2406,6 +2435,9 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
       cand[e] = MODE == kModeSample && live && 4 * q + e < V && bin[e] != 0u && ok(f2key(xs[e]));
       any |= cand[e];
     }
+    if (coded && live)   // written through like the slots (elements past the row are -inf: bin 0)
+      __hip_atomic_store(codes + q, (bin[0] >> 2) | ((bin[1] >> 2) << 8) | ((bin[2] >> 2) << 16) | ((bin[3] >> 2) << 24),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (MODE == kModeSample && any) {
       const uint4 w = philox4x32_10(q, (uint32_t)r, k0, k1);
 #pragma unroll
@@ -2485,77 +2517,191 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
     cut = (int)sm.res[0];
     ma = sm.res64[0];
   }
-  // the cut bin as a key range [ka, kb): nuc_bin is monotone in the value up to m
-  auto first_key = [&](uint32_t b) {        // smallest key <= kmax whose bin is >= b, else kmax + 1
-    uint32_t lo = kKeyNegInf, hi = kmax + 1u;
-    while (lo < hi) {
-      const uint32_t mid = lo + ((hi - lo) >> 1);
-      if (nuc_bin(key2f(mid), nb) >= b) hi = mid;
-      else lo = mid + 1u;
-    }
-    return lo;
+  auto best_of = [&](int g, int b) {        // part g's best packed score in bin b
+    return (uint64_t)__hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + kNucBins + b, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
   };
-  const uint32_t ka = binned ? first_key((uint32_t)cut) : kKeyNegInf;
-  const uint32_t kb = binned ? first_key((uint32_t)cut + 1u) : kKeyNegInf;
-  // one read of the row: the cut bin's tokens into the LDS list; top-p masks also mark the
-  // tokens above the cut that min-p keeps
-  uint8_t* mrow = (MODE == kModeTopp && P.out_mask) ? P.out_mask + (int64_t)r * P.V : nullptr;
-  uint32_t n_up = 0, k_up = 0;
-  // as values: x >= xb is key >= kb, and x >= xa is key >= ka (keys order the values, -0 as +0)
-  const float xa = key2f(ka), xb = key2f(kb);
-  if (binned || MODE == kModeTopp) visit_quads(row, V, 0u, nq, [&](const float4& v, uint32_t q, bool live) {
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-    const float qmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v.x, v.y), __builtin_elementwise_maximum(v.z, v.w));
-    const float qmin = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v.x, v.y), __builtin_elementwise_minimum(v.z, v.w));
-    bool inl[4] = {false, false, false, false};
-    uint32_t nin = 0;
-    if (binned) {
-      // xb > -inf here, so the -inf that pads a quad is never above the cut
+  uint32_t nlist = 0;                       // the cut bin's tokens, listed in (ckey, cidx)
+  bool listed = false;
+  uint64_t bst = 0;                         // sampling: the best packed score above the cut bin
+  if (coded) {
+    // The best score above the cut bin against the cut bin's best: when the former is larger
+    // it is the sample, whichever prefix of the cut bin the cut keeps (the kept tokens of the
+    // cut bin score at most its best), and the cut bin's tokens are not needed.
+    uint64_t bc = 0;
+    for (int i = cut + 1 + (int)threadIdx.x; i < kNucBins; i += kRT)
+      for (int g = 0; g < G; ++g) bst = max(bst, best_of(g, i));
+    if ((int)threadIdx.x < G) bc = best_of((int)threadIdx.x, cut);
+    block_max2_u64(bst, bc, sm.red64);
+    if (bst > bc) {
+      if (threadIdx.x == 0) {
+        const int32_t tok = (int32_t)~(uint32_t)bst;
+        P.out_token[r] = tok;
+        put_logp(P, r, tok, t, lse);
+      }
+      return true;
+    }
+    if (cut >= 4) {
+      // The tokens whose code is the cut bin's (bins 4 * (cut / 4) .. + 3): their ids into the
+      // LDS list (one reservation per wave and word), then their values, kept when their bin is
+      // the cut bin. More than kCodeCap of them: the value scan below instead.
+      const uint32_t want = (uint32_t)cut >> 2;
+      const uint64_t* cw = reinterpret_cast<const uint64_t*>(codes);
+      const uint32_t nw = (nq + 1u) >> 1;   // words of two quads (tokens 8j .. 8j + 7)
+      auto load = [&](uint64_t (&v)[8], uint32_t base) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) n_up += xs[e] >= xb ? 1u : 0u;
-      if (qmax >= xa && qmin < xb) {   // some token of the quad may lie in the cut bin
+        for (int u = 0; u < 8; ++u)
+          v[u] = __hip_atomic_load(cw + min(base + u * kRT + threadIdx.x, nw - 1u), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      };
+      uint64_t v[8];
+      load(v, 0u);
+      for (uint32_t base = 0; base < nw; base += kRT * 8) {
+        uint64_t nx[8];
+        load(nx, base + kRT * 8);        // clamped: in bounds; the next round in flight
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t jw = base + u * kRT + threadIdx.x;
+          uint32_t hits = 0;
+          if (jw < nw) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (2 * jw + (uint32_t)(e >> 2) < nq && (uint32_t)((v[u] >> (8 * e)) & 0xFFu) == want) hits |= 1u << e;
+          }
+          if (__ballot(hits != 0u)) {
+            const uint32_t nh = (uint32_t)__popc(hits);
+            const uint32_t incl = wave_incl_scan(nh);
+            const uint32_t tot = wave_total(incl);
+            uint32_t wb = 0;
+            if (lane() == 0) wb = atomicAdd(&sm.bcount, tot);
+            uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb) + incl - nh;
+            while (hits) {
+              const uint32_t e = (uint32_t)__builtin_ctz(hits);
+              hits &= hits - 1u;
+              if (pos < (uint32_t)kCodeCap) sm.cidx[pos] = 8 * jw + e;
+              ++pos;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = nx[u];
+      }
+      bar();
+      const uint32_t nc = sm.bcount;
+      bar();
+      if (nc <= (uint32_t)kCodeCap) {
+        uint32_t id[kCodePer];
+        float xv[kCodePer];
+#pragma unroll
+        for (int u = 0; u < kCodePer; ++u) {
+          const uint32_t i = u * kRT + threadIdx.x;
+          id[u] = i < nc ? sm.cidx[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kCodePer; ++u) xv[u] = (u * kRT + threadIdx.x < nc && id[u] < V) ? row[id[u]] : -INFINITY;
+        if (threadIdx.x == 0) sm.bcount = 0;
+        bar();                             // every listed id read before the list is rewritten
+#pragma unroll
+        for (int u = 0; u < kCodePer; ++u) {
+          if (u * kRT + threadIdx.x < nc && nuc_bin(xv[u], nb) == (uint32_t)cut) {
+            const uint32_t pos = atomicAdd(&sm.bcount, 1u);
+            sm.ckey[pos] = f2key(xv[u]);
+            sm.cidx[pos] = id[u];
+          }
+        }
+        listed = true;
+      } else if (threadIdx.x == 0) {
+        sm.bcount = 0;
+      }
+      bar();
+      if (listed) {
+        nlist = sm.bcount;
+        bar();
+        if (threadIdx.x == 0) sm.bcount = 0;   // zero again outside the small-bin collections
+        bar();
+      }
+    }
+  }
+  uint32_t un = 0;                          // tokens above the cut bin (top-p masks: min-p's share)
+  uint64_t uk = 0;
+  if (!listed) {
+    // the cut bin as a key range [ka, kb): nuc_bin is monotone in the value up to m
+    auto first_key = [&](uint32_t b) {        // smallest key <= kmax whose bin is >= b, else kmax + 1
+      uint32_t lo = kKeyNegInf, hi = kmax + 1u;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (nuc_bin(key2f(mid), nb) >= b) hi = mid;
+        else lo = mid + 1u;
+      }
+      return lo;
+    };
+    const uint32_t ka = binned ? first_key((uint32_t)cut) : kKeyNegInf;
+    const uint32_t kb = binned ? first_key((uint32_t)cut + 1u) : kKeyNegInf;
+    // one read of the row: the cut bin's tokens into the LDS list; top-p masks also mark the
+    // tokens above the cut that min-p keeps
+    uint8_t* mrow = (MODE == kModeTopp && P.out_mask) ? P.out_mask + (int64_t)r * P.V : nullptr;
+    uint32_t n_up = 0, k_up = 0;
+    // as values: x >= xb is key >= kb, and x >= xa is key >= ka (keys order the values, -0 as +0)
+    const float xa = key2f(ka), xb = key2f(kb);
+    if (binned || MODE == kModeTopp) visit_quads(row, V, 0u, nq, [&](const float4& v, uint32_t q, bool live) {
+      const float xs[4] = {v.x, v.y, v.z, v.w};
+      const float qmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v.x, v.y), __builtin_elementwise_maximum(v.z, v.w));
+      const float qmin = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v.x, v.y), __builtin_elementwise_minimum(v.z, v.w));
+      bool inl[4] = {false, false, false, false};
+      uint32_t nin = 0;
+      if (binned) {
+        // xb > -inf here, so the -inf that pads a quad is never above the cut
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n_up += xs[e] >= xb ? 1u : 0u;
+        if (qmax >= xa && qmin < xb) {   // some token of the quad may lie in the cut bin
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            inl[e] = live && 4 * q + e < V && xs[e] >= xa && xs[e] < xb;
+            nin += inl[e] ? 1u : 0u;
+          }
+        }
+      }
+      if (MODE == kModeTopp && qmax >= xb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          inl[e] = live && 4 * q + e < V && xs[e] >= xa && xs[e] < xb;
-          nin += inl[e] ? 1u : 0u;
+          const bool keep = live && 4 * q + e < V && xs[e] >= xb && ok(f2key(xs[e]));
+          k_up += keep ? 1u : 0u;
+          if (keep && mrow) mrow[4 * q + e] = 1;
         }
       }
-    }
-    if (MODE == kModeTopp && qmax >= xb) {
+      const uint64_t any = __ballot(nin != 0u);
+      if (any) {   // cut-bin tokens: one LDS reservation per wave and round
+        const uint32_t incl = wave_incl_scan(nin);
+        const uint32_t tot = wave_total(incl);
+        uint32_t wb = 0;
+        if (lane() == 0) wb = atomicAdd(&sm.bcount, tot);
+        uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb) + incl - nin;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = live && 4 * q + e < V && xs[e] >= xb && ok(f2key(xs[e]));
-        k_up += keep ? 1u : 0u;
-        if (keep && mrow) mrow[4 * q + e] = 1;
-      }
-    }
-    const uint64_t any = __ballot(nin != 0u);
-    if (any) {   // cut-bin tokens: one LDS reservation per wave and round
-      const uint32_t incl = wave_incl_scan(nin);
-      const uint32_t tot = wave_total(incl);
-      uint32_t wb = 0;
-      if (lane() == 0) wb = atomicAdd(&sm.bcount, tot);
-      uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb) + incl - nin;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (inl[e]) {
-          if (pos < (uint32_t)kLdsCand) {
-            sm.ckey[pos] = f2key(xs[e]);
-            sm.cidx[pos] = 4 * q + e;
+        for (int e = 0; e < 4; ++e) {
+          if (inl[e]) {
+            if (pos < (uint32_t)kLdsCand) {
+              sm.ckey[pos] = f2key(xs[e]);
+              sm.cidx[pos] = 4 * q + e;
+            }
+            ++pos;
           }
-          ++pos;
         }
       }
+    });
+    bar();
+    nlist = sm.bcount;
+    bar();
+    if (threadIdx.x == 0) sm.bcount = 0;   // zero again outside the small-bin collections
+    bar();
+    if (nlist > (uint32_t)kLdsCand) return false;
+    if (MODE == kModeTopp) {
+      uint64_t a = n_up, b = k_up;
+      block_sum2_u64<kRW>(a, b, sm.red64);
+      un = (uint32_t)a;
+      uk = b;
     }
-  });
-  bar();
-  const uint32_t nlist = sm.bcount;
-  bar();
-  if (threadIdx.x == 0) sm.bcount = 0;   // zero again outside the small-bin collections
-  bar();
-  if (nlist > (uint32_t)kLdsCand) return false;
-  uint64_t un = n_up, uk = k_up;
-  block_sum2_u64<kRW>(un, uk, sm.red64);
+  }
   Sel sp = sel_all();
   if (binned) {
     // the exact cut inside the cut bin (a bin is a contiguous key range)
@@ -2568,9 +2714,10 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
     base_key = block_min_u32<kRW>(base_key, sm.red);
     uint32_t kept_unused;
     sp = select_mass<false>(LdsVis{sm.ckey, sm.cidx, nlist}, wmass, target, nlist, top_key, base_key, 0u, V - 1,
-                            sm, kept_unused, false, ma, (uint32_t)un);
+                            sm, kept_unused, false, ma, un);
   }
   if (MODE == kModeTopp) {
+    uint8_t* mrow = P.out_mask ? P.out_mask + (int64_t)r * P.V : nullptr;
     uint64_t c = threadIdx.x == 0 ? uk : 0ull, z = 0;
     for (uint32_t i = threadIdx.x; i < nlist; i += kRT) {
       if (sel_member(sp, sm.ckey[i], sm.cidx[i]) && ok(sm.ckey[i])) {
@@ -2581,12 +2728,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
     block_sum2_u64<kRW>(c, z, sm.red64);
     if (threadIdx.x == 0) P.out_kept[r] = (int32_t)c;
   } else if (MODE == kModeSample) {
-    uint64_t bst = 0;
     if (binned) {
-      for (int i = cut + 1 + (int)threadIdx.x; i < kNucBins; i += kRT)
-        for (int g = 0; g < G; ++g)
-          bst = max(bst, (uint64_t)__hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + kNucBins + i, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
       for (uint32_t i = threadIdx.x; i < nlist; i += kRT) {
         const uint32_t key = sm.ckey[i], id = sm.cidx[i];
         if (sel_member(sp, key, id) && ok(key)) {
@@ -2595,9 +2737,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
         }
       }
     } else {
-      for (int g = threadIdx.x; g < G; g += kRT)
-        bst = max(bst, (uint64_t)__hip_atomic_load(slots + (int64_t)g * 2 * kNucBins + kNucBins, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
+      for (int g = threadIdx.x; g < G; g += kRT) bst = max(bst, best_of(g, 0));
     }
     uint32_t hi = (uint32_t)(bst >> 32);
     hi = block_max_u32<kRW>(hi, sm.red);
@@ -3369,8 +3509,11 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   // With a top-k array, rows whose k reaches the row length are seen on the device only: the
   // row kernel then runs up to 8 workgroups per row (one per CU across the batch) that share
   // such rows' nucleus work; for the other rows the extra workgroups end at once.
-  // Each part keeps its bins in a slot of 2 * kNucBins words inside the row's candidate area.
-  const int64_t slots = pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2) / (2 * kNucBins * (int64_t)sizeof(uint64_t));
+  // Each part keeps its bins in a slot of 2 * kNucBins words inside the row's candidate area;
+  // when sampling, the slots are followed by one byte per token (in 8-byte words of two quads).
+  const int64_t code_bytes = MODE == kModeSample ? ((V + 3) / 4 + 1) / 2 * (int64_t)sizeof(uint64_t) : 0;
+  const int64_t slots = (pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2) - code_bytes) /
+                        (2 * kNucBins * (int64_t)sizeof(uint64_t));
   const int64_t split = std::min<int64_t>({8, std::max<int64_t>(1, kSplitCUs / rows), slots});
   P.split = (MODE != kModeTopk && !P.direct && !P.force_exact && k != nullptr && (p != nullptr || minp != nullptr) && split > 0)
                 ? (int32_t)split : 0;
