@@ -26,6 +26,9 @@ extern "C" {
  *                         alone, the row loaded straight into its LDS (one launch instead of
  *                         two); 0 = such rows also take the stream kernel. A forced chunk size
  *                         also turns it off.
+ *   TS_KNOB_NUCLEUS_PASSES 1 = sampling calls without a top-k array always take the nucleus
+ *                         passes for their top-p / min-p rows; 0 (default) = calls of at most
+ *                         6,400,000 logits over rows of at most 100,000 take the split nucleus.
  * Every setting gives byte-identical results, with two exceptions under TS_KNOB_DIRECT: a
  * full-row sample (top-k and top-p off) rounds its perturbed scores in another order, so its
  * token can differ where two scores lie within a few fp32 ulps, and the LSE of
@@ -35,6 +38,7 @@ extern "C" {
 #define TS_KNOB_CHUNK_ELEMS   1
 #define TS_KNOB_FORCE_EXACT   2
 #define TS_KNOB_DIRECT        3
+#define TS_KNOB_NUCLEUS_PASSES 4
 int64_t ts_debug_set(int knob, int64_t value);
 
 #ifdef __cplusplus

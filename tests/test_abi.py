@@ -95,6 +95,8 @@ def test_status_strings_and_knobs(lib):
     assert lib.ts_debug_set(ts.TS_KNOB_CHUNK_ELEMS, 0) == 2048
     big = lib.ts_workspace_bytes(ts.TS_OP_SAMPLE_ROWS, 4, 100000, 0)
     assert small != big
+    assert lib.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, 1) == 0
+    assert lib.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, 0) == 1
     assert lib.ts_debug_set(99, 1) == -1
 
 

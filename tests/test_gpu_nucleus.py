@@ -27,18 +27,24 @@ def d(a, dt):
 
 
 def both(fn):
-    """fn() with the nucleus pass and with the row-streaming path."""
+    """fn() with the nucleus passes (forced for every call size) and with the row-streaming
+    path; a third run with the default routing (small sampling calls take the split nucleus)
+    must give the same bytes as the first."""
     torch = torch_cuda()
     out = []
-    for exact in (0, 1):
+    for exact, passes in ((0, 1), (1, 1), (0, 0)):
         old = ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, exact)
+        oldp = ts.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, passes)
         try:
             res = fn()
             torch.cuda.synchronize()
             out.append([None if v is None else host(v) for v in res])
         finally:
             ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, old)
-    return out
+            ts.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, oldp)
+    for a, b in zip(out[0], out[2]):
+        assert (a is None and b is None) or np.array_equal(a, b), "default routing differs from the nucleus passes"
+    return out[:2]
 
 
 def mixed_rows(seed, rows, vocab):

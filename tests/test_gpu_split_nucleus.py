@@ -3,8 +3,9 @@ top-p or min-p on take the row kernel's split nucleus: up to 8 workgroups per ro
 part of the row and draw its window tokens' Gumbel scores, and the last one to finish cuts the
 nucleus. The parts per row follow the batch size (8 for a few rows, 1 from 256 rows up), so the
 row counts below cover 8, 3, 2 and 1 parts. Every output byte must equal the nucleus passes of
-a call without a top-k array and the single-workgroup row-streaming path (forced exact), and
-every row must match the oracle. Rows mix spread logits, bf16-like ties, a narrow near-uniform
+a call without a top-k array (forced), the single-workgroup row-streaming path (forced exact)
+and a call without a top-k array on the default routing (small sampling calls take the split
+nucleus there too), and every row must match the oracle. Rows mix spread logits, bf16-like ties, a narrow near-uniform
 row, masked tokens, heavy ties, a dominant head, and min-p-only rows (p = 1).
 """
 import numpy as np
@@ -48,23 +49,26 @@ def rows_for(seed, rows, vocab):
 
 
 def three_ways(fn):
-    """fn(k or None) with the top-k array (split nucleus), without it (nucleus passes), and
-    with the top-k array on the forced row-streaming path."""
+    """fn(k or None) with the top-k array (split nucleus), without it on the nucleus passes
+    (forced), with the top-k array on the forced row-streaming path, and without it on the
+    default routing (the split nucleus for small sampling calls, else the nucleus passes)."""
     torch = torch_cuda()
     out = []
-    for use_k, exact in ((True, 0), (False, 0), (True, 1)):
+    for use_k, exact, passes in ((True, 0, 0), (False, 0, 1), (True, 1, 0), (False, 0, 0)):
         old = ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, exact)
+        oldp = ts.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, passes)
         try:
             res = fn(use_k)
             torch.cuda.synchronize()
             out.append([None if v is None else host(v) for v in res])
         finally:
             ts.ts_debug_set(ts.TS_KNOB_FORCE_EXACT, old)
+            ts.ts_debug_set(ts.TS_KNOB_NUCLEUS_PASSES, oldp)
     return out
 
 
 def same(outs, what):
-    for j in (1, 2):
+    for j in (1, 2, 3):
         for a, b in zip(outs[0], outs[j]):
             assert np.array_equal(a, b), f"{what}: split differs from path {j}"
 

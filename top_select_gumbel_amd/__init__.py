@@ -36,6 +36,7 @@ TS_OP_SAMPLE_ROWS = 2
 TS_KNOB_CHUNK_ELEMS = 1
 TS_KNOB_FORCE_EXACT = 2
 TS_KNOB_DIRECT = 3
+TS_KNOB_NUCLEUS_PASSES = 4
 
 EXPORTED = (
     "ts_workspace_bytes", "ts_workspace_init", "ts_topk_select", "ts_topk_select_rows", "ts_topp_mask",

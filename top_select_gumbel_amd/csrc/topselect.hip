@@ -131,6 +131,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // lives in the row's candidate slices, which nucleus rows leave unused).
 constexpr int kSplitCUs = 256;   // row-kernel workgroups that fill the chip (one per CU: its LDS)
 constexpr int kNucBins = 1024;   // nucleus bins (value-linear window below the maximum, and bin 0)
+constexpr int64_t kSplitNokV = 100000;         // calls without a top-k array: the split nucleus
+constexpr int64_t kSplitNokLogits = 6400000;   // for rows up to this long, calls up to this size
 constexpr int kCodeCap = 4096;   // split nucleus: tokens sharing the cut bin's code, listed at most
 constexpr int kCodePer = kCodeCap / kRT;
 struct NucRow {
@@ -249,8 +251,9 @@ __device__ __forceinline__ RowPlan plan_row(const Params& P, int mode, int r) {
   return rp;
 }
 
-// Rows of the row kernel's split nucleus: calls with a top-k array whose value for the row
-// reaches the row length (top-k off, visible on the device only), with top-p or min-p on.
+// Rows of the row kernel's split nucleus: rows with top-p or min-p on and top-k off, in calls
+// with a top-k array (whose value for the row reaches the row length, visible on the device
+// only) and in small sampling calls without one that the host sends here.
 __device__ __forceinline__ bool split_row(const Params& P, const RowPlan& rp) {
   return P.split && rp.path == kPathStream && rp.k_eff >= rp.n && (rp.p != 1.0f || rp.minp > 0.0f);
 }
@@ -2370,7 +2373,8 @@ __device__ __forceinline__ void block_max2_u64(uint64_t& a, uint64_t& b, uint64_
 
 // Top-p (and min-p after it) over whole rows whose k reaches the row length, in calls with a
 // top-k array (the host cannot see the array's values, so the nucleus passes over the chunk
-// workgroups do not run for them). The row kernel runs P.split workgroups per row; each takes
+// workgroups do not run for them) and in small sampling calls without one (fewer launches than
+// the nucleus passes). The row kernel runs P.split workgroups per row; each takes
 // a contiguous part of the row and, with the row maximum m known from the wave summaries:
 //  - bins every token's exact fixed-point mass by value in the window below m (nuc_bin; bin 0
 //    below the window, summed in registers);
@@ -3417,6 +3421,7 @@ using tsh::fail;
 thread_local int64_t g_knob_chunk = 0;
 thread_local int64_t g_knob_exact = 0;
 thread_local int64_t g_knob_direct = 1;
+thread_local int64_t g_knob_nucleus = 0;
 
 struct Plan {
   int64_t chunks = 0, chunk_len = 0, cap_w = 0;
@@ -3503,20 +3508,25 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   P.force_exact = (int32_t)g_knob_exact;
   // Rows that fit the row kernel's LDS skip the stream kernel (unless a chunk size is forced).
   P.direct = (V <= kLdsCand && g_knob_chunk == 0 && g_knob_direct != 0) ? 1 : 0;
-  // No top-k array: every row has top-k off, so rows with top-p or min-p on take the
-  // nucleus pass (spread over the chunk workgroups) instead of one workgroup streaming the row.
-  P.nucleus = (MODE != kModeTopk && !P.direct && !P.force_exact && k == nullptr && (p != nullptr || minp != nullptr)) ? 1 : 0;
   // With a top-k array, rows whose k reaches the row length are seen on the device only: the
   // row kernel then runs up to 8 workgroups per row (one per CU across the batch) that share
-  // such rows' nucleus work; for the other rows the extra workgroups end at once.
-  // Each part keeps its bins in a slot of 2 * kNucBins words inside the row's candidate area;
-  // when sampling, the slots are followed by one byte per token (in 8-byte words of two quads).
+  // such rows' nucleus work (the split nucleus); for the other rows the extra workgroups end
+  // at once. Each part keeps its bins in a slot of 2 * kNucBins words inside the row's
+  // candidate area; when sampling, the slots are followed by one byte per token (in 8-byte
+  // words of two quads).
   const int64_t code_bytes = MODE == kModeSample ? ((V + 3) / 4 + 1) / 2 * (int64_t)sizeof(uint64_t) : 0;
   const int64_t slots = (pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2) - code_bytes) /
                         (2 * kNucBins * (int64_t)sizeof(uint64_t));
   const int64_t split = std::min<int64_t>({8, std::max<int64_t>(1, kSplitCUs / rows), slots});
-  P.split = (MODE != kModeTopk && !P.direct && !P.force_exact && k != nullptr && (p != nullptr || minp != nullptr) && split > 0)
-                ? (int32_t)split : 0;
+  const bool nucleus_on = MODE != kModeTopk && !P.direct && !P.force_exact && (p != nullptr || minp != nullptr);
+  // No top-k array: every row has top-k off, so rows with top-p or min-p on take the nucleus
+  // passes (spread over the chunk workgroups, two launches more) or, when sampling in a call of
+  // at most kSplitNokLogits logits over rows of at most kSplitNokV, the split nucleus, which is
+  // faster there (fewer launches; the passes' wider grid wins on larger calls).
+  const bool nok_split = MODE == kModeSample && k == nullptr && V <= kSplitNokV &&
+                         (int64_t)rows * V <= kSplitNokLogits && split > 0 && g_knob_nucleus == 0;
+  P.nucleus = (nucleus_on && k == nullptr && !nok_split) ? 1 : 0;
+  P.split = (nucleus_on && (k != nullptr || nok_split) && split > 0) ? (int32_t)split : 0;
   const unsigned row_grid = (unsigned)(rows * (P.split ? P.split : 1));
   P.out_idx = out_idx;
   P.out_kept = out_kept;
@@ -3758,6 +3768,11 @@ int64_t ts_debug_set(int knob, int64_t value) {
     case TS_KNOB_DIRECT: {
       const int64_t old = g_knob_direct;
       g_knob_direct = value ? 1 : 0;
+      return old;
+    }
+    case TS_KNOB_NUCLEUS_PASSES: {
+      const int64_t old = g_knob_nucleus;
+      g_knob_nucleus = value ? 1 : 0;
       return old;
     }
     default: return -1;
