@@ -743,11 +743,15 @@ __device__ __forceinline__ Sel select_mass(const KVis& kvis, const WMass& wmass,
 
 // ------------------------------------------------------------------ misc helpers
 
+// The perturbed score (x - m) / T + g of token idx, with 1 / T rounded once per row (the
+// same reciprocal on every path, so every path forms the same score; a correctly rounded
+// division per token costs ten vector instructions). The compiler hoists 1.0f / t out of the
+// callers' loops.
 __device__ __forceinline__ float gumbel_score(uint32_t key, uint32_t idx, float m, float t,
                                               uint32_t r, uint32_t k0, uint32_t k1) {
   const uint4 w = philox4x32_10(idx >> 2, r, k0, k1);
   const float g = gumbel_from_uniform(uniform_from_word(pick_word(w, idx & 3u)));
-  return (key2f(key) - m) / t + g;
+  return (key2f(key) - m) * (1.0f / t) + g;
 }
 
 
@@ -2448,7 +2452,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
       for (int e = 0; e < 4; ++e) {
         if (cand[e]) {
           const float g = gumbel_from_uniform(uniform_from_word(pick_word(w, (uint32_t)e)));
-          const float sc = (xs[e] - m) / t + g;
+          const float sc = (xs[e] - m) * (1.0f / t) + g;   // as gumbel_score
           const uint64_t pk = ((uint64_t)f2key(sc) << 32) | (uint32_t)~(4 * q + e);
           if (binned) atomicMax((unsigned long long*)&bbest[bin[e]], (unsigned long long)pk);
           else best = max(best, pk);
@@ -3079,7 +3083,7 @@ __global__ __launch_bounds__(kRT) void ts_row_kernel(Params P) {
       } else {
         for (int i = threadIdx.x; i < nseg; i += kRT) {
           const WaveInfo wi = inf[i];
-          const float adj = wi.best_s + (key2f(wi.kmax) - m) / rp.t;
+          const float adj = wi.best_s + (key2f(wi.kmax) - m) * (1.0f / rp.t);
           if (adj > bs || (adj == bs && wi.best_idx < bi)) { bs = adj; bi = wi.best_idx; }
         }
       }
