@@ -8,7 +8,8 @@ leftovers in the shared scratch. Both batches include tie-heavy rows whose waves
 candidates than the allocation-free slices hold, so those rows take the exact path there, and
 rows whose top-k entry reaches the vocabulary, which take the split nucleus (its parts' slots
 live in the candidate area, so the smaller allocation-free slices give the second batch fewer
-parts per row: 3 against 8).
+parts per row: 3 against 8, and hold no per-token bin codes beside them: there the cut bin's
+tokens come from the row's values, against the codes of the workspace entry point).
 """
 import ctypes
 

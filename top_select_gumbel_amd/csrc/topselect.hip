@@ -168,6 +168,7 @@ struct Params {
   int32_t direct;              // rows of <= kLdsCand logits: the row kernel alone, row in LDS
   int32_t nucleus;             // top-k off for every row: the nucleus pass spreads top-p work
   int32_t split;               // workgroups per row of the row kernel's split nucleus (0: none)
+  int32_t codes;               // split nucleus, sampling: the parts store per-token bin codes
   struct NucRow* nuc;          // per row: the nucleus pass's histograms
   int32_t* out_idx;
   int32_t* out_kept;
@@ -2423,7 +2424,8 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   // row), in one word per quad after the parts' slots, so that the finishing workgroup can find
   // the cut bin's tokens without reading the row's values (a quarter of the bytes).
   uint32_t* const codes = reinterpret_cast<uint32_t*>(slots + (int64_t)G * 2 * kNucBins);
-  const bool coded = MODE == kModeSample && binned;
+  const bool scored = MODE == kModeSample && binned;   // the parts keep the best score per bin
+  const bool coded = scored && P.codes != 0;           // and store the codes (when they fit)
 
   // ---- this workgroup's part: masses by bin, and the best score per bin
   uint64_t z0 = 0, best = 0;
@@ -2532,7 +2534,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
   uint32_t nlist = 0;                       // the cut bin's tokens, listed in (ckey, cidx)
   bool listed = false;
   uint64_t bst = 0;                         // sampling: the best packed score above the cut bin
-  if (coded) {
+  if (scored) {
     // The best score above the cut bin against the cut bin's best: when the former is larger
     // it is the sample, whichever prefix of the cut bin the cut keeps (the kept tokens of the
     // cut bin score at most its best), and the cut bin's tokens are not needed.
@@ -2549,7 +2551,7 @@ __device__ __forceinline__ bool row_nucleus(const Params& P, const RowPlan& rp, 
       }
       return true;
     }
-    if (cut >= 4) {
+    if (coded && cut >= 4) {
       // The tokens whose code is the cut bin's (bins 4 * (cut / 4) .. + 3): their ids into the
       // LDS list (one reservation per wave and word), then their values, kept when their bin is
       // the cut bin. More than kCodeCap of them: the value scan below instead.
@@ -3517,10 +3519,14 @@ int launch(const float* x, int64_t rows, int64_t V, int64_t stride, const int32_
   // such rows' nucleus work (the split nucleus); for the other rows the extra workgroups end
   // at once. Each part keeps its bins in a slot of 2 * kNucBins words inside the row's
   // candidate area; when sampling, the slots are followed by one byte per token (in 8-byte
-  // words of two quads).
-  const int64_t code_bytes = MODE == kModeSample ? ((V + 3) / 4 + 1) / 2 * (int64_t)sizeof(uint64_t) : 0;
-  const int64_t slots = (pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2) - code_bytes) /
-                        (2 * kNucBins * (int64_t)sizeof(uint64_t));
+  // words of two quads) if the area holds them beside at least one slot (the
+  // allocation-free entry point's smaller slices do not: its parts then store no codes, and a
+  // cut bin's tokens come from the row's values).
+  const int64_t area = pl.chunks * kW1 * pl.cap_w * (int64_t)sizeof(uint2);
+  const int64_t slot_bytes = 2 * kNucBins * (int64_t)sizeof(uint64_t);
+  const int64_t code_bytes = ((V + 3) / 4 + 1) / 2 * (int64_t)sizeof(uint64_t);
+  P.codes = (MODE == kModeSample && area - code_bytes >= slot_bytes) ? 1 : 0;
+  const int64_t slots = (area - (P.codes ? code_bytes : 0)) / slot_bytes;
   const int64_t split = std::min<int64_t>({8, std::max<int64_t>(1, kSplitCUs / rows), slots});
   const bool nucleus_on = MODE != kModeTopk && !P.direct && !P.force_exact && (p != nullptr || minp != nullptr);
   // No top-k array: every row has top-k off, so rows with top-p or min-p on take the nucleus
