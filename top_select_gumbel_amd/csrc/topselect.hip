@@ -2021,7 +2021,8 @@ __device__ __forceinline__ uint32_t nuc_bin(float x, const NucBin& nb) {
   return min(1u + (uint32_t)f, (uint32_t)(kNucBins - 1));
 }
 
-constexpr int kNT = 512;   // threads of the histogram pass (its LDS allows 4 workgroups per CU)
+constexpr int kNT = 256;   // threads of the histogram pass: 8 workgroups per CU, so a decode grid
+                           // (1216) is resident at once (with 512, 1024 are and 192 wait)
 struct SmemN {
   uint64_t mass[kNucBins];
   uint32_t red[4 * (kNT / 64)];
