@@ -6,7 +6,8 @@ ts_sample_rows_minp and ts_sample_rows_logp; the sampled tokens, the statuses an
 counts must match the oracle on every row. Cases vary the batch (1-40 rows: 8 down to 6 parts
 per row), the vocabulary (12,289-100,000, ragged quads) and the rows: spread logits at four
 scales, exact ties, masked tokens, dominant heads, a narrow near-uniform row, an all-equal row,
-greedy rows, min-p-only rows, and NaN or +inf rows (status codes).
+greedy rows, min-p-only rows, and NaN or +inf rows (status codes); every fourth case calls the
+min-p entry point with no top-p array.
 """
 import numpy as np
 import pytest
@@ -79,7 +80,8 @@ def test_split_sweep_without_top_k_array(i):
     kv = dev(np.full(rows, v, np.int32))
     banner(f"{label}: sample, min-p, logp")
     tok, st = four_ways(lambda use_k: ts.ts_sample_rows(xs, kv if use_k else None, pd, td, sd))
-    four_ways(lambda use_k: ts.ts_sample_rows_minp(xs, kv if use_k else None, pd, td, md, sd))
+    pm = None if i % 4 == 1 else pd                                        # min-p alone: no top-p array
+    four_ways(lambda use_k: ts.ts_sample_rows_minp(xs, kv if use_k else None, pm, td, md, sd))
     lt, _, _, _ = four_ways(lambda use_k: ts.ts_sample_rows_logp(xs, kv if use_k else None, pd, td, sd))
     assert np.array_equal(lt, tok), "the logprob entry point samples the same tokens"
     banner(f"{label}: oracle")
